@@ -1,0 +1,1 @@
+"""CPU float64 oracle (test infrastructure only; never imported by the product path)."""

@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks an oracle function against a hand-worked fixture, a brute
+force, an exact-arithmetic special case, a closed form or an independent
+construction (pure-Python loops, an explicit token-level mask, finite
+differences), chosen so that a dropped term, a flipped comparison or a
+transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import bsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ints(s):
+    s = s.strip()
+    return [] if s == "-" else [int(t) for t in s.split()]
+
+
+# ----------------------------------------------------------------------------
+# Top-p
+# ----------------------------------------------------------------------------
+
+def test_top_p_hand_worked_fixture():
+    rows = [ln for ln in open(os.path.join(GOLDEN, "top_p_hand_worked.txt")) if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 10
+    for ln in rows:
+        cand, weights, p, forced, expect = ln.split("|")
+        cand = np.array(_ints(cand))
+        logits = np.log(np.array([float(t) for t in weights.split()]))
+        sel = O.top_p_select(cand, logits, float(p), np.array(_ints(forced), dtype=np.int64))
+        assert sel.selected.tolist() == _ints(expect), ln
+
+
+def _brute_force_top_p(logits, p):
+    """Smallest subset with probability mass >= p; then largest mass; then lowest ids."""
+    n = len(logits)
+    w = [math.exp(s) for s in logits]
+    z = sum(w)
+    prob = [x / z for x in w]
+    for size in range(1, n + 1):
+        best = None
+        for sub in itertools.combinations(range(n), size):
+            m = sum(prob[j] for j in sub)
+            if m >= p and (best is None or m > best[0] + 1e-12):
+                best = (m, sub)
+        if best is not None:
+            return sorted(best[1]), prob
+    return list(range(n)), prob
+
+
+def _subset_margin(prob, p):
+    n = len(prob)
+    return min(abs(sum(prob[j] for j in sub) - p)
+               for size in range(1, n + 1) for sub in itertools.combinations(range(n), size))
+
+
+def test_top_p_brute_force_small_rows():
+    rng = np.random.default_rng(11)
+    checked = 0
+    while checked < 200:
+        n = int(rng.integers(1, 11))
+        logits = rng.normal(0, 1.5, n)
+        p = float(rng.uniform(0.05, 0.99))
+        expect, prob = _brute_force_top_p(logits.tolist(), p)
+        if _subset_margin(prob, p) < 1e-9:
+            continue
+        got = O.top_p_select(np.arange(n), logits, p)
+        assert got.selected.tolist() == expect
+        checked += 1
+
+
+def test_top_p_coverage_invariant():
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        n = int(rng.integers(2, 200))
+        logits = rng.normal(0, 3, n)
+        p = float(rng.uniform(0.1, 0.999))
+        r = O.top_p_select(np.arange(n), logits, p)
+        prob = np.exp(logits - logits.max())
+        prob /= prob.sum()
+        kept = prob[r.selected].sum()
+        assert kept >= p - 1e-12
+        # dropping the lowest-ranked kept block falls below p
+        last = r.ranked[r.k_star - 1]
+        assert kept - prob[last] < p
+        # every kept block outranks every dropped one
+        dropped = np.setdiff1d(np.arange(n), r.selected)
+        if dropped.size:
+            assert logits[r.selected].min() >= logits[dropped].max()
+
+
+def test_top_p_exact_uniform_ties_and_inclusive_cut():
+    # K = 0 makes every pooled logit exactly 0: probabilities are exactly 1/16.
+    N, bs, D = 1024, 64, 64
+    q = np.random.default_rng(3).normal(size=(N, D))
+    k = np.zeros((N, D))
+    rows = O.estimate_head(q, k, bs, float(np.float32(0.9)), 0.125)
+    for r in rows:
+        assert r.selected.tolist() == list(range(15))       # 14/16 < 0.9 <= 15/16
+    rows = O.estimate_head(q, k, bs, 0.875, 0.125)
+    for r in rows:
+        assert r.selected.tolist() == list(range(14))       # C_14 = 14/16 == p: inclusive cut
+
+
+def test_top_p_duplicated_key_block_resolves_to_lower_index():
+    # Constant tokens per block: pooled logit of key block j is exactly c_j.
+    D, bs = 16, 8
+    u = np.zeros(D)
+    u[0] = 1.0
+    c = [2.0, 1.0, 0.0, 1.0]               # blocks 1 and 3 are identical
+    k = np.concatenate([np.tile(cj * u, (bs, 1)) for cj in c])
+    q = np.tile(4.0 * u, (4 * bs, 1))      # scale = 1/4 -> logit = c_j
+    # probabilities e^2, e, 1, e over Z: C_1 = 0.534, C_2 = 0.731, C_3 = 0.928
+    sel = O.estimate_head(q, k, bs, 0.6, 0.25)[0].selected.tolist()
+    assert sel == [0, 1]
+    sel = O.estimate_head(q, k, bs, 0.8, 0.25)[0].selected.tolist()
+    assert sel == [0, 1, 3]
+    sel = O.estimate_head(q, k, bs, 0.95, 0.25)[0].selected.tolist()
+    assert sel == [0, 1, 2, 3]
+
+
+def test_forced_prefix_blocks_join_after_the_cut():
+    rng = np.random.default_rng(4)
+    q = rng.normal(size=(300, 8))
+    k = rng.normal(size=(300, 8))
+    plain = O.estimate_head(q, k, 64, 0.5, 0.35)
+    forced = O.estimate_head(q, k, 64, 0.5, 0.35, keep_prefix_tokens=70)   # tokens 0..69: blocks 0, 1
+    for a, b in zip(plain, forced):
+        assert b.k_star == a.k_star
+        assert b.selected.tolist() == sorted(set(a.selected.tolist()) | {0, 1})
+    assert O.forced_blocks(64, 64, 5).tolist() == [0]
+    assert O.forced_blocks(65, 64, 5).tolist() == [0, 1]
+    assert O.forced_blocks(0, 64, 5).tolist() == []
+
+
+def test_candidate_restriction():
+    rng = np.random.default_rng(5)
+    N, bs = 700, 64
+    q = rng.normal(size=(N, 16))
+    k = rng.normal(size=(N, 16)) + q
+    nb = O.num_blocks(N, bs)
+    full = O.estimate_head(q, k, bs, 0.8, 0.25)
+    same = O.estimate_head(q, k, bs, 0.8, 0.25, candidate_rows=[np.arange(nb)] * nb)
+    assert [r.selected.tolist() for r in full] == [r.selected.tolist() for r in same]
+    cands = [np.sort(rng.choice(nb, size=int(rng.integers(1, nb)), replace=False)) for _ in range(nb)]
+    sub = O.estimate_head(q, k, bs, 0.8, 0.25, candidate_rows=cands, keep_prefix_tokens=10)
+    qb, kb = O.pool_blocks(q, bs), O.pool_blocks(k, bs)
+    for i, r in enumerate(sub):
+        assert set(r.selected.tolist()) <= set(cands[i].tolist()) | {0}
+        # same answer as a full-row softmax with non-candidates at -inf
+        s = 0.25 * (qb[i] @ kb.T)
+        s_masked = np.full(nb, -np.inf)
+        s_masked[cands[i]] = s[cands[i]]
+        e = np.exp(s_masked - s_masked.max())
+        prob = e / e.sum()
+        order = sorted(range(nb), key=lambda j: (-s_masked[j], j))
+        acc, keep = 0.0, []
+        for j in order:
+            keep.append(j)
+            acc += prob[j]
+            if acc >= 0.8:
+                break
+        assert r.selected.tolist() == sorted(set(keep) | {0})
+    empty = O.estimate_head(q, k, bs, 0.8, 0.25, candidate_rows=[np.zeros(0)] * nb)
+    assert all(r.selected.size == 0 for r in empty)
+
+
+# ----------------------------------------------------------------------------
+# pooling
+# ----------------------------------------------------------------------------
+
+def test_pool_blocks_matches_loop_on_ragged_tail():
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(37, 3))
+    got = O.pool_blocks(x, 8)
+    assert got.shape == (5, 3)
+    for i in range(5):
+        toks = [t for t in range(37) if t // 8 == i]
+        for d in range(3):
+            assert got[i, d] == pytest.approx(sum(x[t, d] for t in toks) / len(toks), abs=1e-14)
+    assert len(toks) == 5
+
+
+# ----------------------------------------------------------------------------
+# sparse attention
+# ----------------------------------------------------------------------------
+
+def _dense_reference(q, k, v, scale):
+    s = scale * q @ k.T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    lse = np.log(np.exp(s).sum(axis=1))
+    return p @ v, lse, p
+
+
+def test_all_blocks_equals_dense_softmax_attention():
+    rng = np.random.default_rng(7)
+    B, H, N, D, bs = 1, 2, 200, 16, 64
+    Q, K, V = (rng.normal(size=(B, H, N, D)) for _ in range(3))
+    scale = 1 / math.sqrt(D)
+    row_ptr, col_idx, _ = O.estimate_mask(Q, K, bs, 1.0, scale)
+    nb = O.num_blocks(N, bs)
+    assert np.diff(row_ptr).tolist() == [nb] * (B * H * nb)
+    Ob, L, M = O.sparse_forward(Q, K, V, bs, row_ptr, col_idx, scale)
+    for h in range(H):
+        o, lse, p = _dense_reference(Q[0, h], K[0, h], V[0, h], scale)
+        assert np.abs(Ob[0, h] - o).max() < 1e-12
+        assert np.abs(L[0, h] - lse).max() < 1e-12
+        for i in range(nb):
+            r = h * nb + i
+            qs = slice(i * bs, min((i + 1) * bs, N))
+            for e in range(row_ptr[r], row_ptr[r + 1]):
+                j = col_idx[e]
+                ks = slice(j * bs, min((j + 1) * bs, N))
+                assert M[e] == pytest.approx(p[qs, ks].sum(axis=1).mean(), abs=1e-12)
+
+
+def _random_mask(rng, B, H, nb, empty_rows=True):
+    rows = []
+    for _ in range(B * H * nb):
+        if empty_rows and rng.random() < 0.1:
+            rows.append(np.zeros(0, np.int64))
+        else:
+            rows.append(np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False)))
+    return O.rows_to_csr(rows)
+
+
+def test_block_mask_equals_explicit_token_mask():
+    rng = np.random.default_rng(8)
+    B, H, N, D, bs = 2, 2, 150, 8, 32        # 5 blocks, last one holds 22 tokens
+    Q, K, V = (rng.normal(size=(B, H, N, D)) for _ in range(3))
+    nb = O.num_blocks(N, bs)
+    row_ptr, col_idx = _random_mask(rng, B, H, nb)
+    scale = 0.3
+    Ob, L, M = O.sparse_forward(Q, K, V, bs, row_ptr, col_idx, scale)
+    for b in range(B):
+        for h in range(H):
+            allow = np.zeros((N, N), bool)
+            for i in range(nb):
+                r = (b * H + h) * nb + i
+                for j in col_idx[row_ptr[r]:row_ptr[r + 1]]:
+                    allow[i * bs:(i + 1) * bs, j * bs:(j + 1) * bs] = True
+            s = np.where(allow, scale * Q[b, h] @ K[b, h].T, -np.inf)
+            has = allow.any(axis=1)
+            m = np.where(has, s.max(axis=1), 0.0)
+            e = np.exp(s - m[:, None])
+            z = e.sum(axis=1)
+            p = np.divide(e, z[:, None], out=np.zeros_like(e), where=has[:, None])
+            assert np.abs(Ob[b, h] - p @ V[b, h]).max() < 1e-12
+            lse = np.where(has, m + np.log(np.where(has, z, 1.0)), -np.inf)
+            assert np.array_equal(np.isinf(L[b, h]), ~has)
+            assert np.abs(L[b, h][has] - lse[has]).max() < 1e-12
+            for i in range(nb):
+                r = (b * H + h) * nb + i
+                for e_ in range(row_ptr[r], row_ptr[r + 1]):
+                    j = col_idx[e_]
+                    blk = p[i * bs:(i + 1) * bs, j * bs:(j + 1) * bs]
+                    assert M[e_] == pytest.approx(blk.sum(axis=1).mean(), abs=1e-12)
+
+
+def test_tiny_case_against_pure_python_loops():
+    rng = np.random.default_rng(9)
+    N, D, bs = 11, 3, 4                        # blocks of 4, 4, 3 tokens
+    q, k, v = (rng.normal(size=(N, D)) for _ in range(3))
+    rows = [np.array([0, 2]), np.array([1]), np.array([0, 1, 2])]
+    row_ptr, col_idx = O.rows_to_csr(rows)
+    scale = 0.7
+    Ob, L, M = O.sparse_forward(q[None, None], k[None, None], v[None, None], bs, row_ptr, col_idx, scale)
+    for t in range(N):
+        i = t // bs
+        keys = [u for j in rows[i] for u in range(j * bs, min(j * bs + bs, N))]
+        logit = {u: scale * sum(q[t, d] * k[u, d] for d in range(D)) for u in keys}
+        z = sum(math.exp(logit[u]) for u in keys)
+        assert L[0, 0, t] == pytest.approx(math.log(z), abs=1e-13)
+        for d in range(D):
+            o = sum(math.exp(logit[u]) / z * v[u, d] for u in keys)
+            assert Ob[0, 0, t, d] == pytest.approx(o, abs=1e-13)
+    # mass of (block 0, key block 2): mean over 4 queries of the probability on tokens 8..10
+    want = 0.0
+    for t in range(4):
+        keys = list(range(0, 4)) + list(range(8, 11))
+        w = [math.exp(scale * sum(q[t, d] * k[u, d] for d in range(D))) for u in keys]
+        want += sum(w[4:]) / sum(w) / 4
+    assert M[1] == pytest.approx(want, abs=1e-13)
+
+
+def test_mass_rows_sum_to_one_and_empty_rows():
+    rng = np.random.default_rng(10)
+    B, H, N, D, bs = 1, 3, 300, 8, 64
+    Q, K, V = (rng.normal(size=(B, H, N, D)) for _ in range(3))
+    nb = O.num_blocks(N, bs)
+    row_ptr, col_idx = _random_mask(rng, B, H, nb)
+    Ob, L, M = O.sparse_forward(Q, K, V, bs, row_ptr, col_idx, 0.4)
+    assert (M >= 0).all()
+    for r in range(B * H * nb):
+        a, b = row_ptr[r], row_ptr[r + 1]
+        h, i = divmod(r, nb)
+        span = slice(i * bs, min(i * bs + bs, N))
+        if a == b:
+            assert (Ob[0, h, span] == 0).all() and np.isneginf(L[0, h, span]).all()
+        else:
+            assert M[a:b].sum() == pytest.approx(1.0, abs=1e-12)
+
+
+def test_executed_pairs_counts_valid_token_pairs():
+    rng = np.random.default_rng(13)
+    N, bs, B, H = 150, 32, 1, 2
+    nb = O.num_blocks(N, bs)
+    row_ptr, col_idx = _random_mask(rng, B, H, nb)
+    want = 0
+    for r in range(B * H * nb):
+        i = r % nb
+        nq = min(bs, N - i * bs)
+        want += sum(nq * min(bs, N - j * bs) for j in col_idx[row_ptr[r]:row_ptr[r + 1]])
+    assert O.executed_pairs(N, bs, B, H, row_ptr, col_idx) == want
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+
+def test_backward_matches_central_finite_differences():
+    rng = np.random.default_rng(14)
+    B, H, N, D, bs = 1, 1, 10, 3, 4
+    Q, K, V, G = (rng.normal(size=(B, H, N, D)) for _ in range(4))
+    rows = [np.array([0, 2]), np.array([1, 2]), np.array([0, 1, 2])]
+    row_ptr, col_idx = O.rows_to_csr(rows)
+    scale = 0.6
+    dQ, dK, dV = O.sparse_backward(Q, K, V, G, bs, row_ptr, col_idx, scale)
+
+    def loss(q, k, v):
+        o, _, _ = O.sparse_forward(q, k, v, bs, row_ptr, col_idx, scale)
+        return float((o * G).sum())
+
+    h = 1e-6
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        for t in range(N):
+            for d in range(D):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][0, 0, t, d] += h
+                up = loss(*args)
+                args[which][0, 0, t, d] -= 2 * h
+                dn = loss(*args)
+                fd = (up - dn) / (2 * h)
+                assert abs(fd - grad[0, 0, t, d]) <= 1e-6 * max(1.0, abs(fd)), (which, t, d)
+
+
+def test_backward_dv_closed_form_and_zero_row_sums():
+    rng = np.random.default_rng(15)
+    B, H, N, D, bs = 1, 1, 90, 5, 32
+    Q, K, V, G = (rng.normal(size=(B, H, N, D)) for _ in range(4))
+    nb = O.num_blocks(N, bs)
+    row_ptr, col_idx = _random_mask(rng, B, H, nb)
+    scale = 0.5
+    dQ, dK, dV = O.sparse_backward(Q, K, V, G, bs, row_ptr, col_idx, scale)
+    allow = np.zeros((N, N), bool)
+    for i in range(nb):
+        for j in col_idx[row_ptr[i]:row_ptr[i + 1]]:
+            allow[i * bs:(i + 1) * bs, j * bs:(j + 1) * bs] = True
+    s = np.where(allow, scale * Q[0, 0] @ K[0, 0].T, -np.inf)
+    has = allow.any(axis=1)
+    e = np.exp(s - np.where(has, s.max(axis=1), 0.0)[:, None])
+    p = np.divide(e, e.sum(axis=1)[:, None], out=np.zeros_like(e), where=has[:, None])
+    assert np.abs(dV[0, 0] - p.T @ G[0, 0]).max() < 1e-12
+    # dS rows sum to zero, so sum_k dS[q,k] * (K_k + c) is independent of c:
+    # shifting every key by a constant vector leaves dQ unchanged.
+    shift = rng.normal(size=D)
+    dQ2, _, _ = O.sparse_backward(Q, K + shift, V, G, bs, row_ptr, col_idx, scale)
+    # the shift changes the logits by scale*q.shift per query row, which the
+    # softmax removes, so P (and dS) are unchanged and dQ moves by scale*dS@shift = 0
+    assert np.abs(dQ2 - dQ).max() < 1e-10
