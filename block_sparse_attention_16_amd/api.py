@@ -1,0 +1,185 @@
+"""Torch-facing wrappers with the C ABI's names (bsa_estimate_mask, bsa_forward, ...).
+
+Argument marshalling only: shapes, dtypes and devices are checked, outputs and
+workspaces are allocated as torch tensors when the caller does not pass them,
+and the call goes to libbsa.so on torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_FORWARD, BsaCsr, BsaShape,
+                   check, load)
+
+
+@dataclass
+class Csr:
+    """Block mask: row_ptr [R+1] and col_idx [capacity], int32 device tensors."""
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+
+    @property
+    def capacity(self) -> int:
+        return self.col_idx.numel()
+
+    def c(self) -> BsaCsr:
+        return BsaCsr(self.row_ptr.data_ptr(), self.col_idx.data_ptr() if self.capacity else None, self.capacity)
+
+    def nnz(self) -> int:
+        """Total selected blocks (reads row_ptr[R]; synchronises)."""
+        return int(self.row_ptr[-1].item())
+
+    def to_host(self):
+        """(row_ptr, col_idx[:nnz]) as int64 numpy arrays."""
+        rp = self.row_ptr.cpu().numpy().astype("int64")
+        n = min(int(rp[-1]), self.capacity)
+        return rp, self.col_idx[:n].cpu().numpy().astype("int64")
+
+
+def csr_from_host(row_ptr, col_idx, device, capacity: int | None = None) -> Csr:
+    rp = torch.as_tensor(row_ptr, dtype=torch.int32).to(device)
+    ci = torch.as_tensor(col_idx, dtype=torch.int32)
+    cap = ci.numel() if capacity is None else capacity
+    buf = torch.zeros(max(cap, 1), dtype=torch.int32)
+    buf[: min(cap, ci.numel())] = ci[:cap]
+    return Csr(rp, buf[:cap].to(device) if cap else buf[:0].to(device))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def make_shape(B: int, H: int, N: int, D: int, block: int, dtype: int) -> BsaShape:
+    return BsaShape(B, H, N, D, block, dtype)
+
+
+def _shape_of(q: torch.Tensor, block: int) -> BsaShape:
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    return make_shape(B, H, N, D, block, _dtype_code(q))
+
+
+def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def bsa_workspace_size(shape: BsaShape, kind: int, capacity: int = 0) -> int:
+    return int(load().bsa_workspace_size(ctypes.byref(shape), kind, capacity))
+
+
+def _workspace(shape: BsaShape, kind: int, capacity: int, ws: torch.Tensor | None, device) -> torch.Tensor:
+    need = bsa_workspace_size(shape, kind, capacity)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def num_rows(q: torch.Tensor, block: int) -> int:
+    B, H, N, _ = q.shape
+    return B * H * (-(-N // block))
+
+
+def bsa_estimate_mask(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: float = 0.0,
+                      candidate: Csr | None = None, keep_prefix_tokens: int = 0, out: Csr | None = None,
+                      capacity: int | None = None, workspace: torch.Tensor | None = None) -> Csr:
+    """Block-importance estimator -> CSR mask (see bsa_estimate_mask in include/bsa.h)."""
+    _check(q, "q")
+    _check(k, "k", like=q)
+    shape = _shape_of(q, block)
+    nb = -(-q.shape[2] // block)
+    R = num_rows(q, block)
+    if out is None:
+        cap = R * nb if capacity is None else capacity
+        out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
+                  torch.empty(cap, dtype=torch.int32, device=q.device))
+    ws = _workspace(shape, BSA_WS_ESTIMATE, 0, workspace, q.device)
+    cand = ctypes.byref(candidate.c()) if candidate is not None else None
+    oc = out.c()
+    st = load().bsa_estimate_mask(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p), float(scale), cand,
+                                  int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(), _stream())
+    check(st, "bsa_estimate_mask")
+    return out
+
+
+def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Csr, block: int, scale: float = 0.0,
+                want_mass: bool = True, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                mass: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Sparse attention forward -> (O, LSE, block mass or None)."""
+    _check(q, "q")
+    _check(k, "k", like=q)
+    _check(v, "v", like=q)
+    shape = _shape_of(q, block)
+    B, H, N, D = q.shape
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", like=q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lse, "lse", dtype=torch.float32)
+    if want_mass and mass is None:
+        mass = torch.empty(max(mask.capacity, 1), dtype=torch.float32, device=q.device)
+    if mass is not None:
+        _check(mass, "mass", dtype=torch.float32)
+        if mass.numel() < mask.capacity:
+            raise ValueError("mass must hold mask.capacity entries")
+    ws = _workspace(shape, BSA_WS_FORWARD, mask.capacity, workspace, q.device)
+    mc = mask.c()
+    st = load().bsa_forward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), float(scale),
+                            ctypes.byref(mc), o.data_ptr(), lse.data_ptr(), _ptr(mass), ws.data_ptr(), ws.numel(),
+                            _stream())
+    check(st, "bsa_forward")
+    return o, lse, (mass[: mask.capacity] if mass is not None else None)
+
+
+def bsa_backward(q, k, v, o, d_o, lse, mask: Csr, block: int, scale: float = 0.0,
+                 workspace: torch.Tensor | None = None, dq=None, dk=None, dv=None):
+    """Backward of bsa_forward for dL/dO = d_o -> (dQ, dK, dV)."""
+    _check(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _check(t, n, like=q)
+    _check(lse, "lse", dtype=torch.float32)
+    shape = _shape_of(q, block)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws = _workspace(shape, BSA_WS_BACKWARD, mask.capacity, workspace, q.device)
+    mc = mask.c()
+    st = load().bsa_backward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             d_o.data_ptr(), lse.data_ptr(), float(scale), ctypes.byref(mc), dq.data_ptr(),
+                             dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    check(st, "bsa_backward")
+    return dq, dk, dv
+
+
+def bsa_status_string(status: int) -> str:
+    return load().bsa_status_string(status).decode()
+
+
+def bsa_last_error() -> str:
+    return load().bsa_last_error().decode()
+
+
+def bsa_version() -> int:
+    return int(load().bsa_version())

@@ -1,0 +1,77 @@
+// Internal declarations shared by the host API and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// Problem description after host-side validation.
+struct Problem {
+  int B, H, N, D, bs, nb, R;     // R = B*H*nb mask rows
+  int dtype;                     // bsa_dtype
+  size_t elem;                   // bytes per element of q/k/v/o
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace carving: every sub-buffer starts on a 256-byte boundary.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// ---- estimator (estimate.hip) ----
+struct EstimateWs {
+  float* qbar;       // [R, D] pooled query means
+  float* kbar;       // [R, D] pooled key means
+  int32_t* counts;   // [R] selected blocks per row
+  uint32_t* bits;    // [R, words] selection bitmask
+  int words;         // ceil(nb / 32)
+};
+EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes);
+hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
+                           const bsa_csr* cand, int keep_prefix_tokens, const bsa_csr* out,
+                           const EstimateWs& w, hipStream_t s);
+
+// ---- forward (forward_bf16.hip, forward_fp32.hip) ----
+struct ForwardWs {
+  void* vt;          // bf16 path: V transposed per block, [B*H, nb, D, bs] (keys permuted)
+  float* part;       // [capacity, 2, bs] per-entry partial log2-sum-exp (block mass)
+};
+ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes);
+hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
+                               const bsa_csr* mask, void* o, float* lse, float* mass,
+                               const ForwardWs& w, hipStream_t s);
+hipError_t launch_forward_fp32(const Problem& p, const void* q, const void* k, const void* v, float scale,
+                               const bsa_csr* mask, void* o, float* lse, float* mass,
+                               const ForwardWs& w, hipStream_t s);
+
+// ---- backward (backward.hip) ----
+struct BackwardWs {
+  float* delta;        // [B*H*N] rowsum(dO * O)
+  int32_t* csc_ptr;    // [B*H*nb + 1] key-major transpose of the mask
+  int32_t* csc_row;    // [capacity] query block of each transposed entry
+  int32_t* csc_cnt;    // [B*H*nb] fill counters
+  void* vt;            // bf16 path: V transposed per block (as the forward)
+  void* qt;            // bf16 path: Q transposed per block
+  void* dot;           // bf16 path: dO transposed per block
+  void* kt;            // bf16 path: K transposed per block
+};
+BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes);
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, float scale, const bsa_csr* mask,
+                           void* dq, void* dk, void* dv, const BackwardWs& w, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,151 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) dynamic block-sparse attention library.
+ *
+ * The library computes, on one GPU, the two-stage estimate-then-attend scheme
+ * for video diffusion transformers:
+ *
+ *   1. a block-importance estimator: mean-pool Q and K over each token block,
+ *      score every (query block, key block) pair with the pooled dot product,
+ *      take a softmax over each query block's row and keep, per row, the
+ *      fewest highest-scoring key blocks whose probability reaches top_p.
+ *      Two-stage estimation of critical key-value pairs: DSV page, Abstract.
+ *      Top-p selection: GSRS page ("Sparse Attention for Video Generation
+ *      Acceleration via Growing Sparsity and Reduced Search"), Abstract.
+ *      Restricting a later search to an earlier step's blocks ("reduced
+ *      search"): GSRS page, Abstract and Figure 4 caption.
+ *   2. a FlashAttention-style forward over the selected key blocks that also
+ *      returns the exact attention mass of every selected block (the block-
+ *      level attention map of the GSRS page, Figure 3 caption, computed inside
+ *      the attention kernel as the GSRS abstract describes), and
+ *   3. the matching backward pass (dQ, dK, dV) over the same block mask, for
+ *      training with dynamic sparsity (DSV page, Abstract).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, D] device
+ *     arrays of the dtype in bsa_shape (bf16 or fp32); LSE is [B, H, N] fp32.
+ *   - Token block i of a sequence covers tokens [i*block, min((i+1)*block, N));
+ *     nb = ceil(N / block) query blocks = key blocks; the last one may be
+ *     partial.  Mask rows are ordered r = (b*H + h)*nb + i; R = B*H*nb.
+ *   - Every pointer is a device pointer owned by the caller.  The library
+ *     never allocates or frees device memory and never synchronises the host;
+ *     all work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns an error status and enqueues nothing.  A HIP launch
+ *     error returns BSA_ERR_HIP.  No C++ exception crosses this interface.
+ *     bsa_last_error() describes the latest failure on the calling thread.
+ *   - Supported: D in {64, 128}, block in {64, 128}, nb <= 4096, B*H*N*D < 2^31.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, p outside (0,1], ... */
+  BSA_ERR_UNSUPPORTED = 2,   /* D, block or dtype the kernels are not built for */
+  BSA_ERR_WORKSPACE = 3,     /* workspace or CSR capacity too small */
+  BSA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_FP32 = 1 } bsa_dtype;
+
+/* Problem shape.  dtype selects the element type of every [B,H,N,D] tensor:
+ * BSA_BF16 is the production path (bf16 MFMA, fp32 accumulation);
+ * BSA_FP32 is the debug path (fp32 arithmetic throughout). */
+typedef struct {
+  int32_t B, H, N, D, block;
+  int32_t dtype; /* bsa_dtype */
+} bsa_shape;
+
+/* Block mask in CSR form over the R mask rows.
+ *   row_ptr [R+1]  int32, row_ptr[0] = 0, non-decreasing; row r's key blocks
+ *                  are col_idx[row_ptr[r] .. row_ptr[r+1]).
+ *   col_idx [capacity] int32 key-block ids, strictly ascending within a row.
+ *   capacity       number of int32 slots col_idx (and a block_mass array)
+ *                  can hold.  R*nb always suffices.
+ * Kernels never touch col_idx at or beyond capacity: entries there are
+ * ignored, and ids outside [0, nb) are ignored. */
+typedef struct {
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int64_t capacity;
+} bsa_csr;
+
+/* Which call a workspace is sized for. */
+typedef enum { BSA_WS_ESTIMATE = 0, BSA_WS_FORWARD = 1, BSA_WS_BACKWARD = 2 } bsa_ws_kind;
+
+/* Bytes of device workspace `kind` needs for `shape` and a CSR of `capacity`
+ * entries (the forward stores per-entry partial sums for the block mass).
+ * Returns 0 for an invalid shape. */
+size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity);
+
+/* Block-importance estimator (see the header comment, stage 1).
+ *   q, k       [B,H,N,D] device tensors of shape->dtype.
+ *   top_p      in (0, 1]; 1 keeps every candidate block.
+ *   scale      score temperature; <= 0 selects 1/sqrt(D) (the attention scale).
+ *   candidate  NULL: every key block is scored.  Otherwise a CSR over the same
+ *              R rows; row r scores, softmaxes and ranks only its candidate
+ *              blocks (reduced search).  An empty candidate row selects only
+ *              the forced blocks.  Must not alias `out`.
+ *   keep_prefix_tokens  in [0, N]: key blocks j with j*block < keep_prefix_tokens
+ *              (e.g. a text prefix) join every row after the Top-p cut.
+ *   out        CSR written by the call.  out->row_ptr receives exact offsets
+ *              even when the total exceeds out->capacity; entries past the
+ *              capacity are dropped, so a caller checks row_ptr[R] <= capacity.
+ *   ws         device workspace of at least
+ *              bsa_workspace_size(shape, BSA_WS_ESTIMATE, 0) bytes.
+ * Ranking is by pooled logit, larger first, lower block id first on ties; the
+ * kept prefix is the shortest whose fp32 cumulative probability reaches top_p.
+ * Each output row is ascending. */
+bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* k,
+                             float top_p, float scale, const bsa_csr* candidate,
+                             int32_t keep_prefix_tokens, bsa_csr* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention forward over a block mask (see the header comment, stage 2).
+ *   q, k, v    [B,H,N,D] device tensors of shape->dtype.
+ *   scale      logit scale; <= 0 selects 1/sqrt(D).
+ *   mask       CSR over the R rows (e.g. from bsa_estimate_mask).
+ *   o          [B,H,N,D] output of shape->dtype: softmax(scale*Q_i K_S^T) V_S
+ *              over the keys S of the row's selected blocks.
+ *   lse        [B,H,N] fp32 output: natural log of sum over S of exp(scale*q.k).
+ *              A row with no selected block gets O = 0 and lse = -inf.
+ *   block_mass NULL, or [mask->capacity] fp32 output aligned with col_idx:
+ *              for entry (i, j), the mean over the valid queries of block i of
+ *              the softmax probability that falls on key block j (each row
+ *              sums to 1).
+ *   ws         at least bsa_workspace_size(shape, BSA_WS_FORWARD, capacity) bytes. */
+bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v,
+                       float scale, const bsa_csr* mask, void* o, float* lse,
+                       float* block_mass, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the sparse forward for a loss L with dL/dO = d_o.
+ *   o, lse     the forward's outputs for the same q, k, v, scale and mask.
+ *   dq, dk, dv [B,H,N,D] outputs of shape->dtype (overwritten, not accumulated).
+ *   ws         at least bsa_workspace_size(shape, BSA_WS_BACKWARD, capacity) bytes.
+ * Deterministic: no floating-point atomics. */
+bsa_status bsa_backward(const bsa_shape* shape, const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse, float scale,
+                        const bsa_csr* mask, void* dq, void* dk, void* dv,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* bsa_status_string(bsa_status status);
+
+/* Message for the most recent failed call on the calling thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

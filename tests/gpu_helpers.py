@@ -1,0 +1,99 @@
+"""Shared pieces of the GPU parity tests: moving seeded inputs to the device and
+comparing the HIP path's outputs with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import bsa_oracle as O
+from workloads import bf16_bits
+
+# Tolerances.  bf16: 1e-2 on O (2e-2 on gradients) for the arithmetic, plus the
+# rounding of the bf16 store itself (at most 2^-9 |x| with ties to even).
+TOL = {
+    "bf16": {"o": 1e-2, "grad": 2e-2, "lse": 1e-3, "mass": 1e-4, "store_rel": 2.0 ** -9},
+    "fp32": {"o": 1e-5, "grad": 1e-5, "lse": 1e-5, "mass": 1e-5, "store_rel": 0.0},
+}
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+def default_scale(D: int) -> float:
+    return f32(1.0 / np.sqrt(D))
+
+
+def compare_masks(rp_gpu, ci_gpu, sels: dict, H: int, nb: int, top_p: float, candidate_rows=None):
+    """Checks every oracle row against the GPU CSR outside the selection band.
+
+    Returns (rows, mismatched rows, band blocks).  Also checks that each GPU row
+    is strictly ascending, in range and inside candidates + forced blocks.
+    """
+    bad, band_total, rows = [], 0, 0
+    for (b, h), sel_rows in sels.items():
+        for i, row in enumerate(sel_rows):
+            r = (b * H + h) * nb + i
+            g = ci_gpu[rp_gpu[r]:rp_gpu[r + 1]]
+            assert np.all(np.diff(g) > 0), f"row {r} not strictly ascending"
+            assert g.size == 0 or (g.min() >= 0 and g.max() < nb)
+            allowed = set(row.candidates.tolist()) | set(row.forced.tolist())
+            assert set(g.tolist()) <= allowed, f"row {r} selects outside candidates"
+            band = O.selection_band(row, top_p)
+            band_total += len(band)
+            if set(g.tolist()) - band != set(row.selected.tolist()) - band:
+                bad.append(r)
+            rows += 1
+    return rows, bad, band_total
+
+
+def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass_gpu, dtype: str):
+    """Oracle on the GPU's own mask for the listed rows; returns the max errors."""
+    tol = TOL[dtype]
+    Oo, Lo, Mo = O.sparse_forward(Qh, Kh, Vh, block, rp, ci, scale, rows=rows)
+    B, H, N, D = Qh.shape
+    nb = O.num_blocks(N, block)
+    err = {"o": 0.0, "o_excess": 0.0, "lse": 0.0, "mass": 0.0}
+    for r in rows:
+        bh, i = divmod(r, nb)
+        b, h = divmod(bh, H)
+        lo, hi = i * block, min(i * block + block, N)
+        og, oo = o_gpu[b, h, lo:hi], Oo[b, h, lo:hi]
+        diff = np.abs(og - oo)
+        err["o"] = max(err["o"], float(diff.max()))
+        err["o_excess"] = max(err["o_excess"], float((diff - tol["o"] - tol["store_rel"] * np.abs(oo)).max()))
+        lg, lo_ = lse_gpu[b, h, lo:hi], Lo[b, h, lo:hi]
+        fin = np.isfinite(lo_)
+        assert np.array_equal(np.isfinite(lg), fin), f"row {r}: -inf pattern of LSE differs"
+        if fin.any():
+            err["lse"] = max(err["lse"], float(np.abs(lg[fin] - lo_[fin]).max()))
+        a, z = rp[r], min(rp[r + 1], ci.size)
+        if mass_gpu is not None and z > a:
+            err["mass"] = max(err["mass"], float(np.abs(mass_gpu[a:z] - Mo[a:z]).max()))
+    return err
+
+
+def assert_forward_within(err: dict, dtype: str, what: str = ""):
+    tol = TOL[dtype]
+    assert err["o_excess"] <= 0.0, f"{what} O error {err['o']:.3g} beyond {tol['o']} (+ bf16 store rounding)"
+    assert err["lse"] <= tol["lse"], f"{what} LSE error {err['lse']:.3g} > {tol['lse']}"
+    assert err["mass"] <= tol["mass"], f"{what} mass error {err['mass']:.3g} > {tol['mass']}"
+
+
+def sample_rows(R: int, nb: int, count: int, seed: int = 0) -> list[int]:
+    """Rows to check against the oracle: the first and last block of the first
+    and last head (ragged tail), plus a seeded random sample."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, nb - 1, R - nb, R - 1}
+    extra = rng.choice(R, size=min(count, R), replace=False).tolist()
+    return sorted(fixed | set(extra))

@@ -1,0 +1,118 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from block_sparse_attention_16_amd import _lib
+
+needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbsa.so not built")
+
+FAKE = 0x10000      # a 16-byte aligned address that validation never dereferences
+
+
+def _shape(**kw):
+    s = dict(B=1, H=2, N=1024, D=64, block=64, dtype=_lib.BSA_BF16)
+    s.update(kw)
+    return _lib.BsaShape(**s)
+
+
+def _csr(cap=1024):
+    return _lib.BsaCsr(FAKE, FAKE + 4096, cap)
+
+
+@needs_lib
+def test_library_exports_every_header_function():
+    names = _lib.header_functions()
+    assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error",
+                            "bsa_status_string", "bsa_version", "bsa_workspace_size"])
+    L = _lib.load()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+@needs_lib
+def test_status_strings_and_version():
+    L = _lib.load()
+    assert L.bsa_status_string(0) == b"ok"
+    assert L.bsa_status_string(3) == b"workspace or capacity too small"
+    assert L.bsa_version() >= 100
+
+
+@needs_lib
+def test_workspace_sizes():
+    L = _lib.load()
+    s = _shape()
+    est = L.bsa_workspace_size(ctypes.byref(s), 0, 0)
+    R, D, nb = 2 * 16, 64, 16
+    assert est >= 2 * R * D * 4 + R * 4 + R * 4
+    fwd = L.bsa_workspace_size(ctypes.byref(s), 1, 100)
+    assert fwd >= 100 * 2 * 64 * 4 + R * nb * 64 * 64 * 2 // nb
+    assert L.bsa_workspace_size(ctypes.byref(_shape(D=96)), 0, 0) == 0
+    assert L.bsa_workspace_size(ctypes.byref(s), 7, 0) == 0
+
+
+def _est(L, shape, q=FAKE, k=FAKE, p=0.9, scale=0.0, cand=None, keep=0, out=None, ws=FAKE, ws_bytes=1 << 30):
+    out = out if out is not None else _csr()
+    return L.bsa_estimate_mask(ctypes.byref(shape), q, k, p, scale, ctypes.byref(cand) if cand else None, keep,
+                               ctypes.byref(out), ws, ws_bytes, None)
+
+
+@needs_lib
+def test_estimate_validation():
+    L = _lib.load()
+    s = _shape()
+    assert _est(L, s, q=None) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, q=FAKE + 2) == _lib.BSA_ERR_INVALID_ARG          # misaligned
+    assert _est(L, s, p=0.0) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, p=1.5) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, p=float("nan")) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, scale=float("inf")) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, keep=-1) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, keep=1025) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, s, ws_bytes=16) == _lib.BSA_ERR_WORKSPACE
+    assert b"workspace" in L.bsa_last_error()
+    assert _est(L, _shape(D=96)) == _lib.BSA_ERR_UNSUPPORTED
+    assert _est(L, _shape(block=32)) == _lib.BSA_ERR_UNSUPPORTED
+    assert _est(L, _shape(dtype=5)) == _lib.BSA_ERR_UNSUPPORTED
+    assert _est(L, _shape(N=0)) == _lib.BSA_ERR_INVALID_ARG
+    assert _est(L, _shape(N=64 * 4097)) == _lib.BSA_ERR_UNSUPPORTED   # more than 4096 blocks
+    out = _csr()
+    assert _est(L, s, cand=out, out=out) == _lib.BSA_ERR_INVALID_ARG   # candidate aliases out
+    bad = _lib.BsaCsr(FAKE, None, 10)
+    assert _est(L, s, out=bad) == _lib.BSA_ERR_INVALID_ARG
+    neg = _lib.BsaCsr(FAKE, FAKE, -1)
+    assert _est(L, s, out=neg) == _lib.BSA_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_forward_and_backward_validation():
+    L = _lib.load()
+    s = _shape()
+    m = _csr()
+    args = [FAKE] * 3
+    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == _lib.BSA_ERR_WORKSPACE
+    st = L.bsa_forward(ctypes.byref(s), FAKE, None, FAKE, 0.0, ctypes.byref(m), FAKE, FAKE, None, FAKE, 1 << 30,
+                       None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0.0, ctypes.byref(m), FAKE, FAKE,
+                        FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_backward(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, ctypes.byref(m), FAKE,
+                        FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

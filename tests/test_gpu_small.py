@@ -1,0 +1,216 @@
+"""GPU parity on the tiny workload and on edge cases, through the C ABI (libbsa.so)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import bsa_oracle as O
+from workloads import get, make_inputs, round_to_bf16
+from tests.gpu_helpers import (TOL, assert_forward_within, compare_forward, compare_masks, default_scale, f32,
+                               to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_16_amd as m
+    m.load()
+    return m
+
+
+def _inputs(rng, B, H, N, D, dtype, scale_q=1.0):
+    q = rng.normal(size=(B, H, N, D)).astype(np.float32) * scale_q
+    k = rng.normal(size=(B, H, N, D)).astype(np.float32)
+    v = rng.normal(size=(B, H, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tiny_workload_end_to_end(bsa, dtype):
+    w = get("tiny")
+    x = make_inputs(w, dtype=dtype)
+    scale, p = default_scale(w.D), f32(w.top_p[0])
+    q, k, v = (to_device(x[n], dtype) for n in "qkv")
+    mask = bsa.bsa_estimate_mask(q, k, p, w.block)
+    o, lse, mass = bsa.bsa_forward(q, k, v, mask, w.block)
+    torch.cuda.synchronize()
+    rp, ci = mask.to_host()
+    _, _, sels = O.estimate_mask(x["q"], x["k"], w.block, p, scale)
+    rows, bad, band = compare_masks(rp, ci, sels, w.H, w.nb, p)
+    assert not bad, f"{len(bad)} of {rows} mask rows differ outside the band"
+    err = compare_forward(x["q"], x["k"], x["v"], w.block, rp, ci, scale, list(range(w.B * w.H * w.nb)),
+                          to_host(o), to_host(lse), to_host(mass), dtype)
+    assert_forward_within(err, dtype, f"tiny {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D,bs", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("N", [1, 37, 200, 700])
+def test_forward_random_masks_ragged(bsa, dtype, D, bs, N):
+    rng = np.random.default_rng(N * 1000 + D + bs)
+    B, H = 1, 2
+    q, k, v = _inputs(rng, B, H, N, D, dtype)
+    nb = O.num_blocks(N, bs)
+    rows = []
+    for r in range(B * H * nb):
+        if r % 5 == 3:
+            rows.append(np.zeros(0, np.int64))                  # empty row
+        else:
+            rows.append(np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False)))
+    rp, ci = O.rows_to_csr(rows)
+    mask = bsa.csr_from_host(rp, ci, "cuda")
+    qd, kd, vd = (to_device(t, dtype) for t in (q, k, v))
+    o, lse, mass = bsa.bsa_forward(qd, kd, vd, mask, bs)
+    torch.cuda.synchronize()
+    scale = default_scale(D)
+    err = compare_forward(q, k, v, bs, rp, ci, scale, list(range(B * H * nb)), to_host(o), to_host(lse),
+                          to_host(mass), dtype)
+    assert_forward_within(err, dtype, f"N={N} D={D} bs={bs}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_all_blocks_is_dense_attention(bsa, dtype):
+    rng = np.random.default_rng(1)
+    B, H, N, D, bs = 1, 2, 300, 64, 64
+    q, k, v = _inputs(rng, B, H, N, D, dtype, scale_q=0.5)
+    qd, kd, vd = (to_device(t, dtype) for t in (q, k, v))
+    mask = bsa.bsa_estimate_mask(qd, kd, 1.0, bs)
+    o, lse, mass = bsa.bsa_forward(qd, kd, vd, mask, bs)
+    torch.cuda.synchronize()
+    rp, ci = mask.to_host()
+    nb = O.num_blocks(N, bs)
+    assert np.array_equal(np.diff(rp), np.full(B * H * nb, nb))
+    scale = default_scale(D)
+    tol = TOL[dtype]
+    for h in range(H):
+        qq, kk, vv = (t[0, h].astype(np.float64) for t in (q, k, v))
+        s = scale * qq @ kk.T
+        pm = np.exp(s - s.max(axis=1, keepdims=True))
+        pm /= pm.sum(axis=1, keepdims=True)
+        dense = pm @ vv
+        og = to_host(o)[0, h]
+        assert (np.abs(og - dense) - tol["o"] - tol["store_rel"] * np.abs(dense)).max() <= 0
+        mg = to_host(mass)
+        for i in range(nb):
+            r = h * nb + i
+            for e in range(rp[r], rp[r + 1]):
+                j = ci[e]
+                want = pm[i * bs:(i + 1) * bs, j * bs:(j + 1) * bs].sum(axis=1).mean()
+                assert abs(mg[e] - want) <= tol["mass"]
+
+
+def test_invalid_ids_and_entries_past_capacity_are_ignored(bsa):
+    rng = np.random.default_rng(2)
+    B, H, N, D, bs = 1, 1, 500, 64, 128
+    q, k, v = _inputs(rng, B, H, N, D, "bf16")
+    nb = O.num_blocks(N, bs)       # 4
+    rows = [np.array([0, 2, 7]), np.array([-1, 1]), np.array([3]), np.array([0, 1, 2, 3])]
+    rp, ci = O.rows_to_csr(rows)
+    cap = 7                         # the last row loses its last two entries
+    mask = bsa.csr_from_host(rp, ci, "cuda", capacity=cap)
+    qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
+    o, lse, mass = bsa.bsa_forward(qd, kd, vd, mask, bs)
+    torch.cuda.synchronize()
+    clean = [np.array([0, 2]), np.array([1]), np.array([3]), np.array([0])]
+    crp, cci = O.rows_to_csr(clean)
+    Oo, Lo, Mo = O.sparse_forward(q, k, v, bs, crp, cci, default_scale(D))
+    og = to_host(o)
+    assert (np.abs(og - Oo) - 1e-2 - 2 ** -9 * np.abs(Oo)).max() <= 0
+    mg = to_host(mass)
+    assert mg[2] == 0.0 and mg[3] == 0.0            # ids 7 and -1
+    assert abs(mg[0] + mg[1] - 1) < 1e-4
+    assert abs(mg[4] - 1) < 1e-4 and abs(mg[5] - 1) < 1e-4 and abs(mg[6] - 1) < 1e-4
+
+
+def test_estimator_capacity_truncation_keeps_exact_offsets(bsa):
+    w = get("tiny")
+    x = make_inputs(w, dtype="bf16")
+    q, k = to_device(x["q"], "bf16"), to_device(x["k"], "bf16")
+    full = bsa.bsa_estimate_mask(q, k, 0.9, w.block)
+    small = bsa.bsa_estimate_mask(q, k, 0.9, w.block, capacity=20)
+    torch.cuda.synchronize()
+    assert torch.equal(full.row_ptr, small.row_ptr)
+    assert full.nnz() > 20
+    assert torch.equal(full.col_idx[:20], small.col_idx)
+
+
+def test_exact_ties_uniform_scores(bsa):
+    # K = 0: every pooled logit is exactly 0 and every probability exactly 1/16.
+    rng = np.random.default_rng(3)
+    q = round_to_bf16(rng.normal(size=(1, 2, 1024, 64)).astype(np.float32))
+    k = np.zeros_like(q)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    for p, expect in ((f32(0.9), list(range(15))), (0.875, list(range(14)))):
+        m = bsa.bsa_estimate_mask(qd, kd, p, 64)
+        rp, ci = m.to_host()
+        for r in range(32):
+            assert ci[rp[r]:rp[r + 1]].tolist() == expect
+
+
+def test_exact_ties_duplicated_key_block(bsa):
+    # constant tokens per block: pooled logit of key block j is exactly c_j
+    D, bs = 64, 64
+    u = np.zeros(D, np.float32)
+    u[0] = 1.0
+    c = [2.0, 1.0, 0.0, 1.0]
+    k = np.concatenate([np.tile(cj * u, (bs, 1)) for cj in c])[None, None]
+    q = np.tile(8.0 * u, (4 * bs, 1))[None, None]          # scale 1/8 -> logit c_j
+    qd, kd = to_device(q.astype(np.float32), "fp32"), to_device(k.astype(np.float32), "fp32")
+    for p, expect in ((0.6, [0, 1]), (0.8, [0, 1, 3]), (0.95, [0, 1, 2, 3])):
+        m = bsa.bsa_estimate_mask(qd, kd, p, bs)
+        rp, ci = m.to_host()
+        assert ci[rp[0]:rp[1]].tolist() == expect
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_candidate_path_and_forced_prefix(bsa, dtype):
+    rng = np.random.default_rng(4)
+    B, H, N, D, bs = 1, 2, 2000, 128, 128
+    q, k, v = _inputs(rng, B, H, N, D, dtype, scale_q=0.3)
+    k = k + q if dtype == "fp32" else round_to_bf16(k + q)
+    nb = O.num_blocks(N, bs)
+    cand_rows = []
+    for r in range(B * H * nb):
+        if r % 7 == 2:
+            cand_rows.append(np.zeros(0, np.int64))
+        else:
+            cand_rows.append(np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False)))
+    crp, cci = O.rows_to_csr(cand_rows)
+    cand = bsa.csr_from_host(crp, cci, "cuda")
+    qd, kd = to_device(q, dtype), to_device(k, dtype)
+    p = f32(0.85)
+    m = bsa.bsa_estimate_mask(qd, kd, p, bs, candidate=cand, keep_prefix_tokens=130)
+    rp, ci = m.to_host()
+    _, _, sels = O.estimate_mask(q, k, bs, p, default_scale(D), candidate=(crp, cci), keep_prefix_tokens=130)
+    rows, bad, band = compare_masks(rp, ci, sels, H, nb, p)
+    assert not bad, f"{len(bad)} of {rows} rows differ"
+    # an empty candidate row keeps only the forced blocks {0, 1}
+    assert ci[rp[2]:rp[3]].tolist() == [0, 1]
+
+
+def test_repeated_calls_are_bitwise_identical(bsa):
+    w = get("tiny")
+    x = make_inputs(w, dtype="bf16")
+    q, k, v = (to_device(x[n], "bf16") for n in "qkv")
+    m1 = bsa.bsa_estimate_mask(q, k, 0.9, w.block)
+    m2 = bsa.bsa_estimate_mask(q, k, 0.9, w.block)
+    o1, l1, s1 = bsa.bsa_forward(q, k, v, m1, w.block)
+    o2, l2, s2 = bsa.bsa_forward(q, k, v, m2, w.block)
+    torch.cuda.synchronize()
+    assert torch.equal(m1.row_ptr, m2.row_ptr) and torch.equal(m1.col_idx[:m1.nnz()], m2.col_idx[:m2.nnz()])
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1[:m1.nnz()], s2[:m2.nnz()])
+
+
+def test_host_validation_errors(bsa):
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_estimate_mask(q, q, 1.5, 64)
+    assert e.value.status == 1
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_estimate_mask(q, q, 0.5, 32)
+    assert e.value.status == 2

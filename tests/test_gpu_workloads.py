@@ -1,0 +1,81 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Masks: every row against the oracle (outside the selection band).  Forward:
+a seeded sample of rows (plus the first/last block of the first/last head),
+each recomputed by the oracle on the GPU's own mask.
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import bsa_oracle as O
+from workloads import get, make_inputs
+from tests.gpu_helpers import (assert_forward_within, compare_forward, compare_masks, default_scale, f32,
+                               sample_rows, to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = int(os.environ.get("BSA_PARITY_SAMPLE_ROWS", "24"))
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_16_amd as m
+    m.load()
+    return m
+
+
+def _run_step(bsa, w, x, top_p, candidate=None, cand_host=None):
+    q, k, v = (to_device(x[n], "bf16") for n in "qkv")
+    mask = bsa.bsa_estimate_mask(q, k, top_p, w.block, candidate=candidate,
+                                 keep_prefix_tokens=w.keep_prefix_tokens)
+    o, lse, mass = bsa.bsa_forward(q, k, v, mask, w.block)
+    torch.cuda.synchronize()
+    rp, ci = mask.to_host()
+    _, _, sels = O.estimate_mask(x["q"], x["k"], w.block, top_p, default_scale(w.D), candidate=cand_host,
+                                 keep_prefix_tokens=w.keep_prefix_tokens)
+    rows, bad, band = compare_masks(rp, ci, sels, w.H, w.nb, top_p)
+    print(f"[{w.name}] p={top_p:.4f} rows={rows} nnz={ci.size} density={ci.size / rows / w.nb:.3f} "
+          f"band={band} mismatched={len(bad)}", flush=True)
+    assert not bad, f"{len(bad)} of {rows} rows differ outside the band: {bad[:10]}"
+    R = w.B * w.H * w.nb
+    sel_rows = sample_rows(R, w.nb, SAMPLE, seed=w.cfg_id)
+    err = compare_forward(x["q"], x["k"], x["v"], w.block, rp, ci, default_scale(w.D), sel_rows,
+                          to_host(o), to_host(lse), to_host(mass), "bf16")
+    print(f"[{w.name}] forward errors on {len(sel_rows)} rows: {err}", flush=True)
+    assert_forward_within(err, "bf16", w.name)
+    return mask, (rp, ci)
+
+
+@pytest.mark.parametrize("name", ["cogvideox", "hunyuan"])
+def test_single_step_workload(bsa, name):
+    w = get(name)
+    x = make_inputs(w, dtype="bf16")
+    _run_step(bsa, w, x, f32(w.top_p[0]))
+
+
+def test_wan_reduced_search_steps(bsa):
+    w = get("wan")
+    first, first_host = None, None
+    for s, p in enumerate(w.top_p, start=1):
+        x = make_inputs(w, step=s, dtype="bf16")
+        mask, host = _run_step(bsa, w, x, f32(p), candidate=first, cand_host=first_host)
+        if s == 1:
+            first, first_host = mask, host
+        else:
+            # every later mask lies inside step 1's blocks
+            rp, ci = host
+            frp, fci = first_host
+            for r in range(0, w.B * w.H * w.nb, 97):
+                assert set(ci[rp[r]:rp[r + 1]].tolist()) <= set(fci[frp[r]:frp[r + 1]].tolist())
+
+
+def test_dsv_training_forward(bsa):
+    w = get("dsv_train")
+    x = make_inputs(w, dtype="bf16", want_grad=False)
+    _run_step(bsa, w, x, f32(w.top_p[0]))
