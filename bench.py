@@ -1,0 +1,233 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of seeded synthetic
+video tokens already resident in HBM: the block-importance estimator
+(mean-pool, pooled scores, row softmax, Top-p, CSR) followed by the sparse
+forward with exact per-block attention mass (and, on the training workload,
+the backward).  Prints one JSON line.
+
+value = executed forward FLOP (4 D sum over selected pairs |Q_i||K_j|) per
+step divided by the step time, in TFLOP/s.  The roofline object reports the
+forward kernel alone, timed with HIP events on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd TFLOP/s (executed + dense-equiv) and % bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+KERNEL_SOURCES = ["block_sparse_attention_16_amd/csrc/forward_bf16.hip"]
+
+
+def executed_pairs(N: int, block: int, BH: int, row_ptr: np.ndarray, col_idx: np.ndarray) -> int:
+    """Sum over selected (i, j) of |Q_i| * |K_j| (valid token pairs)."""
+    nb = -(-N // block)
+    sizes = np.minimum(block, N - np.arange(nb) * block).astype(np.int64)
+    csum = np.concatenate([[0], np.cumsum(sizes[col_idx])])
+    keys_per_row = csum[row_ptr[1:]] - csum[row_ptr[:-1]]
+    return int((np.tile(sizes, BH) * keys_per_row).sum())
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, flop_per_launch: float):
+    """HBM bytes per forward launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "fwd_kernel_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, scale, rp, ci, budget_s: float):
+    """Time the CPU oracle on a seeded sample of mask rows (bounded by budget_s)."""
+    from oracle import bsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    R = w.B * w.H * w.nb
+    order = np.random.default_rng(12345).permutation(R)
+    done, flop, t0 = [], 0.0, time.perf_counter()
+    for r in order:
+        O.sparse_forward(x["q"], x["k"], x["v"], w.block, rp, ci, scale, rows=[int(r)])
+        done.append(int(r))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    sub_rp = np.zeros(len(done) + 1, np.int64)
+    parts = []
+    for n, r in enumerate(done):
+        seg = ci[rp[r]:rp[r + 1]]
+        parts.append(seg)
+        sub_rp[n + 1] = sub_rp[n] + seg.size
+    sizes = np.minimum(w.block, w.N - np.arange(w.nb) * w.block)
+    for n, r in enumerate(done):
+        flop += 4.0 * w.D * sizes[r % w.nb] * sizes[parts[n]].sum()
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(done)} of {R} mask rows (seeded random order), float64 numpy oracle on the GPU's "
+                      f"mask, {dt:.1f} s wall", "seconds": dt, "rows": len(done)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="cogvideox")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards over heads "
+                                   "with no exchange, but no multi-GPU run is part of it)"}))
+        return 2
+
+    import torch
+    import block_sparse_attention_16_amd as bsa
+    from workloads import get, make_inputs, bf16_bits
+
+    w = get(a.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(w, dtype="bf16", want_grad=w.backward)
+
+    def up(arr):
+        return torch.from_numpy(bf16_bits(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    g = up(x["g"]) if w.backward else None
+    top_p = float(np.float32(w.top_p[0]))
+    scale = float(np.float32(1.0 / np.sqrt(w.D)))
+    R = w.B * w.H * w.nb
+    cap = R * w.nb
+    mask = bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int32, device=dev))
+    shape = bsa.make_shape(w.B, w.H, w.N, w.D, w.block, 0)
+    ws_e = torch.empty(bsa.bsa_workspace_size(shape, 0, 0), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(bsa.bsa_workspace_size(shape, 1, cap), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    mass = torch.empty(cap, dtype=torch.float32, device=dev)
+    if w.backward:
+        ws_b = torch.empty(max(bsa.bsa_workspace_size(shape, 2, cap), 256), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record: bool):
+        e0 = torch.cuda.Event(enable_timing=True) if record else None
+        e1 = torch.cuda.Event(enable_timing=True) if record else None
+        e2 = torch.cuda.Event(enable_timing=True) if record else None
+        e3 = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            e0.record(stream)
+        bsa.bsa_estimate_mask(q, k, top_p, w.block, candidate=None, keep_prefix_tokens=w.keep_prefix_tokens,
+                              out=mask, workspace=ws_e)
+        if record:
+            e1.record(stream)
+        bsa.bsa_forward(q, k, v, mask, w.block, out=o, lse=lse, mass=mass, workspace=ws_f)
+        if record:
+            e2.record(stream)
+        if w.backward:
+            bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block, workspace=ws_b, dq=dq, dk=dk, dv=dv)
+        if record:
+            e3.record(stream)
+            ev.append((e0, e1, e2, e3))
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(a.steps):
+        step(True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    est_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _, _ in ev]))
+    fwd_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2, _ in ev]))
+    bwd_ms = float(np.mean([e2.elapsed_time(e3) for _, _, e2, e3 in ev])) if w.backward else None
+
+    rp, ci = mask.to_host()
+    nnz = int(rp[-1])
+    pairs = executed_pairs(w.N, w.block, w.B * w.H, rp, ci)
+    exec_flop = 4.0 * w.D * pairs
+    dense_flop = w.dense_fwd_flop()
+    step_flop = exec_flop * (3.5 if w.backward else 1.0)     # fwd + bwd (2.5x fwd) on the training step
+    value = step_flop / (ms * 1e-3) / 1e12
+    fwd_tflops = exec_flop / (fwd_ms * 1e-3) / 1e12
+    est_bytes = 2.0 * w.B * w.H * w.N * w.D * 2 + 4.0 * (R + 1) + 4.0 * nnz
+    traffic = load_traffic("fwd_kernel", w.name, exec_flop)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "H": w.H, "N": w.N, "D": w.D, "block": w.block,
+                   "top_p": w.top_p[0], "keep_prefix_tokens": w.keep_prefix_tokens,
+                   "step": "estimate + forward(+mass)" + (" + backward" if w.backward else "")},
+        "executed_tflop_per_step": exec_flop / 1e12,
+        "dense_equiv_tflop_per_step": dense_flop / 1e12,
+        "dense_equiv_tflops": round(dense_flop * (3.5 if w.backward else 1.0) / (ms * 1e-3) / 1e12, 3),
+        "fwd_kernel": {"ms": round(fwd_ms, 4), "executed_tflops": round(fwd_tflops, 3),
+                       "dense_equiv_tflops": round(dense_flop / (fwd_ms * 1e-3) / 1e12, 3),
+                       "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
+        "estimator": {"ms": round(est_ms, 4), "algorithmic_bytes": est_bytes,
+                      "gbps": round(est_bytes / (est_ms * 1e-3) / 1e9, 1),
+                      "pct_hbm_peak": round(100 * est_bytes / (est_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)},
+        "block_density": nnz / (R * w.nb),
+        "token_pair_density": pairs / (w.B * w.H * float(w.N) ** 2),
+        "nnz": nnz,
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "fwd_kernel"},
+    }
+    if w.backward:
+        out["bwd_ms"] = round(bwd_ms, 4)
+        out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)
+    if not a.no_cpu_baseline:
+        cb = cpu_baseline(x, w, scale, rp, ci, a.cpu_budget)
+        out["cpu_baseline"] = {k2: cb[k2] for k2 in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

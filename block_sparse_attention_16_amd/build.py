@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["bsa_api.cpp", "estimate.hip", "forward_bf16.hip", "forward_fp32.hip", "backward.hip"]
+SOURCES = ["bsa_api.cpp", "estimate.hip", "forward_bf16.hip", "forward_fp32.hip", "backward.hip",
+           "backward_fp32.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

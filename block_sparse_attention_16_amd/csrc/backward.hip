@@ -1,17 +1,536 @@
-// Sparse attention backward (placeholder until the kernels land).
+// Sparse attention backward over a block mask, bf16 MFMA (gfx950).
+//
+// The DSV page (Abstract) trains video DiTs with dynamic sparse attention;
+// this is the gradient of the sparse forward for a loss with dL/dO = dO,
+// over the same CSR block mask.  With P = exp(scale Q_i K_j^T - LSE):
+//   dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P * (dP - delta),
+//   dQ_i += scale dS K_j,  dK_j += scale dS^T Q_i,  delta_q = dO_q . O_q.
+// Deterministic, no floating-point atomics: dQ is produced query-major over
+// the CSR rows, dK/dV key-major over a transposed (CSC) copy of the mask.
+//
+// Kernels, in launch order:
+//   delta_kernel  delta = rowsum(dO * O) and lse2 = LSE * log2(e), padded per
+//                 head to nb*BS rows (padding: delta 0, lse2 +inf -> P = 0)
+//   csc_kernel    one workgroup per head: counting transpose of the mask, rows
+//                 visited in order so every column lists query blocks ascending
+//   dq_kernel     per query block: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+//   dkv_kernel    per key block:   S = Q K^T,   dP = dO V^T,
+//                 dV^T += dO^T P,  dK^T += Q^T dS
+//
+// MFMA layouts are those of the forward kernel: v_mfma_f32_32x32x16_bf16,
+// operands read from LDS tiles either row-wise (ds_read_b128) or transposed
+// (two ds_read_b64_tr_b16), the 32x32 accumulator of a lane holding one
+// column and 16 rows {8a + 4h + r}, and the k-slot permutation that lets an
+// accumulator, rounded to bf16, feed the next MFMA as its B operand.
 #include "bsa_internal.h"
 
 namespace bsa {
+namespace {
 
-BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes) {
-  (void)p; (void)capacity; (void)ws;
-  *bytes = 0;
-  return BackwardWs{};
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One XOR swizzle of 16-byte chunks that is bank-conflict free both for
+// ds_read_b128 down 16 consecutive rows and for ds_read_b64_tr_b16 over
+// 4 consecutive rows x 4 chunks (rows of CPR = 16 or 8 chunks).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(CPR == 16 || CPR == 8, "row must be 128 or 256 bytes");
+  return CPR == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
-hipError_t launch_backward(const Problem&, const void*, const void*, const void*, const void*, const void*,
-                           const float*, float, const bsa_csr*, void*, void*, void*, const BackwardWs&, hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+}
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int BS, int D>
+struct BCfg {
+  static constexpr int NW = BS / 32;          // waves; wave w owns 32 rows (queries or keys)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int T32 = BS / 32;         // 32-wide tiles per block
+  static constexpr int DS = D / 16, DT = D / 32;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = BS * D * 2;
+  static constexpr int LOADS = TILE_BYTES / (16 * THREADS);
+  static_assert(LOADS * 16 * THREADS == TILE_BYTES, "tile must split evenly over the waves");
+};
+
+// DMA rows [row0, row0 + BS) of two [N, D] bf16 matrices into swizzled LDS
+// tiles (rows past N repeat row N-1).
+template <int BS, int D>
+__device__ __forceinline__ void dma_tiles(const __bf16* __restrict__ a, const __bf16* __restrict__ b, int row0,
+                                          int N, char* ta, char* tb, int wave, int lane) {
+  using C = BCfg<BS, D>;
+#pragma unroll
+  for (int it = 0; it < C::LOADS; ++it) {
+    const int chunk0 = (it * C::NW + wave) * 64;
+    const int L = chunk0 + lane;
+    const int row = L / C::CPR, pos = L % C::CPR;
+    const size_t src = (size_t)min(row0 + row, N - 1) * D + (pos ^ swz<C::CPR>(row)) * 8;
+    lds_dma16(a + src, ta + chunk0 * 16);
+    lds_dma16(b + src, tb + chunk0 * 16);
+  }
+}
+
+// 8 bf16 of row `row`, logical chunk `c`, of a swizzled tile (MFMA A operand).
+template <int CPR>
+__device__ __forceinline__ bf16x8 read_row8(const char* t, int row, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + (row * CPR + (c ^ swz<CPR>(row))) * 16);
+}
+
+// Transposed A operand: lane L receives tile[r0 + 8x + 4(L/32) + t][d0 + L%32]
+// in k-slot 4x + t (the slot order of an accumulator used as B operand).
+template <int CPR>
+__device__ __forceinline__ bf16x8 read_tr8(const char* t, int r0, int d0, int lane) {
+  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
+  const int dcol = d0 + 16 * (G & 1) + 4 * g4;
+  short4_t h[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int row = r0 + 8 * x + 4 * (G >> 1) + tr;
+    h[x] = lds_read_tr16(t + (row * CPR + ((dcol >> 3) ^ swz<CPR>(row))) * 16 + (dcol & 7) * 2);
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const floatx16& a, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)a[half * 8 + e];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O), lse2 = LSE * log2(e); [BH, nb*BS] with padding rows.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                    const float* __restrict__ lse, float* __restrict__ delta,
+                                                    float* __restrict__ lse2, int N, int npad, int BH) {
+  constexpr int LPR = D / 8;                       // lanes per row, 8 elements each
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid / LPR, part = gid % LPR;     // row over BH * npad
+  if (row >= BH * npad) return;
+  const int bh = row / npad, t = row % npad;
+  float s = 0.f;
+  if (t < N) {
+    const size_t off = ((size_t)bh * N + t) * D + part * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)o[off + e] * (float)dout[off + e];
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
+  if (part == 0) {
+    delta[row] = s;
+    lse2[row] = t < N ? lse[(size_t)bh * N + t] * kLog2e : INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// CSC transpose: column (bh, j) lists the query blocks i whose row holds j,
+// ascending; csc_start/csc_count index csc_row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, int64_t cap, int nb,
+                                                  int32_t* __restrict__ csc_start, int32_t* __restrict__ csc_count,
+                                                  int32_t* __restrict__ csc_row) {
+  __shared__ int cnt[4096];
+  __shared__ int cur[4096];
+  __shared__ int wsum[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  auto clampe = [&](int64_t e) { return e < 0 ? (int64_t)0 : (e > cap ? cap : e); };
+  const int64_t hb = clampe(row_ptr[(size_t)bh * nb]), he = clampe(row_ptr[(size_t)bh * nb + nb]);
+  for (int j = tid; j < nb; j += 256) cnt[j] = 0;
+  __syncthreads();
+  for (int64_t e = hb + tid; e < he; e += 256) {
+    const int j = col_idx[e];
+    if (j >= 0 && j < nb) atomicAdd(&cnt[j], 1);
+  }
+  __syncthreads();
+  // exclusive scan of cnt over nb entries: per-thread chunks, then thread totals
+  const int chunk = (nb + 255) / 256;
+  const int c0 = tid * chunk;
+  int run = 0;
+  for (int j = c0; j < c0 + chunk && j < nb; ++j) {
+    const int v = cnt[j];
+    cur[j] = run;
+    run += v;
+  }
+  int x = run;
+  const int lane = tid & 63, w = tid >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int base = (int)hb + x - run;
+  for (int ww = 0; ww < w; ++ww) base += wsum[ww];
+  for (int j = c0; j < c0 + chunk && j < nb; ++j) {
+    cur[j] += base;
+    csc_start[(size_t)bh * nb + j] = cur[j];
+    csc_count[(size_t)bh * nb + j] = cnt[j];
+  }
+  __syncthreads();
+  // fill, one row at a time so each column comes out ascending
+  for (int i = 0; i < nb; ++i) {
+    const int64_t a = clampe(row_ptr[(size_t)bh * nb + i]), b = clampe(row_ptr[(size_t)bh * nb + i + 1]);
+    for (int64_t e = a + tid; e < b; e += 256) {
+      const int j = col_idx[e];
+      if (j >= 0 && j < nb) {
+        const int pos = cur[j];
+        cur[j] = pos + 1;
+        if (pos >= hb && pos < he) csc_row[pos] = i;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per query block (mask row).  Wave w owns queries
+// [32w, 32w+32); per visited key block j (tiles K_j, V_j in LDS):
+//   S^T = K Q^T, P^T = exp2(c2 S^T - lse2_q), dP^T = V dO^T,
+//   dS^T = P^T (dP^T - delta_q), dQ^T += K^T dS^T.
+// ---------------------------------------------------------------------------
+template <int BS, int D>
+__global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
+    __bf16* __restrict__ dq, int N, int nb, float scale) {
+  using C = BCfg<BS, D>;
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
+
+  const int r = blockIdx.x;
+  const int bh = r / nb, i = r - bh * nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int qloc = wave * 32 + l32;
+  const int qq = i * BS + qloc;
+  int64_t e_begin = row_ptr[r], e_end = row_ptr[r + 1];
+  if (e_end > cap) e_end = cap;
+  if (e_begin < 0) e_begin = 0;
+  if (e_begin > e_end) e_begin = e_end;
+  const int n_e = (int)(e_end - e_begin);
+  const __bf16* kh = k + (size_t)bh * N * D;
+  const __bf16* vh = v + (size_t)bh * N * D;
+
+  bf16x8 qf[C::DS], gf[C::DS];     // Q^T and dO^T as B operands (query column qloc)
+  {
+    const int qr = min(qq, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+      qf[ds] = *reinterpret_cast<const bf16x8*>(q + ((size_t)bh * N + qr) * D + ds * 16 + hf * 8);
+      gf[ds] = *reinterpret_cast<const bf16x8*>(dout + ((size_t)bh * N + qr) * D + ds * 16 + hf * 8);
+    }
+  }
+  const size_t prow = (size_t)bh * nb * BS + (size_t)i * BS + qloc;   // padded per-head row
+  const float my_lse2 = lse2[prow];     // +inf for padding queries -> P = 0
+  const float my_delta = delta[prow];
+  const float c2 = scale * kLog2e;
+
+  floatx16 acc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  if (n_e > 0) {
+    const int j0 = col_idx[e_begin];
+    dma_tiles<BS, D>(kh, vh, ((j0 >= 0 && j0 < nb) ? j0 : 0) * BS, N, k0s, v0s, wave, lane);
+  }
+
+  auto do_block = [&](const char* ks, const char* vs, char* kn, char* vn, int it) __attribute__((always_inline)) {
+    const int64_t e = e_begin + it;
+    const int j_raw = col_idx[e];
+    const bool valid = j_raw >= 0 && j_raw < nb;
+    const int j = valid ? j_raw : 0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (it + 1 < n_e) {
+      const int jn = col_idx[e + 1];
+      dma_tiles<BS, D>(kh, vh, ((jn >= 0 && jn < nb) ? jn : 0) * BS, N, kn, vn, wave, lane);
+    }
+    floatx16 st[C::T32], dpt[C::T32];
+#pragma unroll
+    for (int kt = 0; kt < C::T32; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { st[kt][x] = 0.f; dpt[kt][x] = 0.f; }
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+      for (int kt = 0; kt < C::T32; ++kt) {
+        const bf16x8 ka = read_row8<C::CPR>(ks, kt * 32 + l32, ds * 2 + hf);
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ds], st[kt], 0, 0, 0);
+        const bf16x8 va = read_row8<C::CPR>(vs, kt * 32 + l32, ds * 2 + hf);
+        dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ds], dpt[kt], 0, 0, 0);
+      }
+    }
+    bf16x8 dsb[C::T32][2];
+#pragma unroll
+    for (int kt = 0; kt < C::T32; ++kt) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int key = j * BS + kt * 32 + 8 * (x >> 2) + 4 * hf + (x & 3);
+        float p = __builtin_amdgcn_exp2f(fmaf(st[kt][x], c2, -my_lse2));
+        if (!valid || key >= N) p = 0.f;
+        st[kt][x] = p * (dpt[kt][x] - my_delta);
+      }
+      dsb[kt][0] = to_bf16x8(st[kt], 0);
+      dsb[kt][1] = to_bf16x8(st[kt], 1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int kt = 0; kt < C::T32; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 a = read_tr8<C::CPR>(ks, kt * 32 + h2 * 16, dt * 32, lane);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[kt][h2], acc[dt], 0, 0, 0);
+        }
+  };
+
+  for (int it = 0; it < n_e; it += 2) {
+    do_block(k0s, v0s, k1s, v1s, it);
+    if (it + 1 < n_e) do_block(k1s, v1s, k0s, v0s, it + 1);
+  }
+
+  if (qq < N) {
+    __bf16* row = dq + ((size_t)bh * N + qq) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 out4;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) out4[r4] = (__bf16)(acc[dt][g * 4 + r4] * scale);
+        *reinterpret_cast<bf16x4*>(row + dt * 32 + 8 * g + 4 * hf) = out4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per key block (bh, j).  Wave w owns keys
+// [32w, 32w+32); per query block i of column j (tiles Q_i, dO_i in LDS):
+//   S = Q K^T, P = exp2(c2 S - lse2_q), dP = dO V^T, dS = P (dP - delta_q),
+//   dV^T += dO^T P, dK^T += Q^T dS.
+// ---------------------------------------------------------------------------
+template <int BS, int D>
+__global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
+    const int32_t* __restrict__ csc_start, const int32_t* __restrict__ csc_count,
+    const int32_t* __restrict__ csc_row, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, int nb,
+    float scale) {
+  using C = BCfg<BS, D>;
+  __shared__ __attribute__((aligned(1024))) char q0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char q1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char g0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char g1s[C::TILE_BYTES];
+
+  const int c = blockIdx.x;                      // column = bh * nb + j
+  const int bh = c / nb, j = c - bh * nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int kloc = wave * 32 + l32;
+  const int kk = j * BS + kloc;
+  const int start = csc_start[c];
+  const int n_e = csc_count[c];
+  const __bf16* qh = q + (size_t)bh * N * D;
+  const __bf16* gh = dout + (size_t)bh * N * D;
+  const float* lse2h = lse2 + (size_t)bh * nb * BS;
+  const float* delh = delta + (size_t)bh * nb * BS;
+
+  bf16x8 kf[C::DS], vf[C::DS];     // K^T and V^T as B operands (key column kloc)
+  {
+    const int kr = min(kk, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+      kf[ds] = *reinterpret_cast<const bf16x8*>(k + ((size_t)bh * N + kr) * D + ds * 16 + hf * 8);
+      vf[ds] = *reinterpret_cast<const bf16x8*>(v + ((size_t)bh * N + kr) * D + ds * 16 + hf * 8);
+    }
+  }
+  const bool kvalid = kk < N;
+  const float c2 = scale * kLog2e;
+
+  floatx16 adk[C::DT], adv[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { adk[dt][e] = 0.f; adv[dt][e] = 0.f; }
+
+  auto qblock = [&](int it) -> int {
+    const int ib = csc_row[start + it];
+    return (ib >= 0 && ib < nb) ? ib : -1;
+  };
+  if (n_e > 0) {
+    const int i0 = qblock(0);
+    dma_tiles<BS, D>(qh, gh, (i0 < 0 ? 0 : i0) * BS, N, q0s, g0s, wave, lane);
+  }
+
+  auto do_block = [&](const char* qs, const char* gs, char* qn, char* gn, int it) __attribute__((always_inline)) {
+    const int ib = qblock(it);
+    const bool valid = ib >= 0 && kvalid;
+    const int i = ib < 0 ? 0 : ib;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (it + 1 < n_e) {
+      const int in = qblock(it + 1);
+      dma_tiles<BS, D>(qh, gh, (in < 0 ? 0 : in) * BS, N, qn, gn, wave, lane);
+    }
+    // S and dP for every 32-query tile: lane holds key column kloc, query rows
+    floatx16 s[C::T32], dp[C::T32];
+#pragma unroll
+    for (int qt = 0; qt < C::T32; ++qt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { s[qt][x] = 0.f; dp[qt][x] = 0.f; }
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+      for (int qt = 0; qt < C::T32; ++qt) {
+        const bf16x8 qa = read_row8<C::CPR>(qs, qt * 32 + l32, ds * 2 + hf);
+        s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s[qt], 0, 0, 0);
+        const bf16x8 ga = read_row8<C::CPR>(gs, qt * 32 + l32, ds * 2 + hf);
+        dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ds], dp[qt], 0, 0, 0);
+      }
+    }
+    bf16x8 pb[C::T32][2], dsb[C::T32][2];
+#pragma unroll
+    for (int qt = 0; qt < C::T32; ++qt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = i * BS + qt * 32 + 8 * g + 4 * hf;       // 4 consecutive query rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2h + qr);
+        const float4 d4 = *reinterpret_cast<const float4*>(delh + qr);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int x = g * 4 + r4;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[qt][x], c2, -lv[r4]));
+          if (!valid) p = 0.f;
+          s[qt][x] = p;
+          dp[qt][x] = p * (dp[qt][x] - dv4[r4]);
+        }
+      }
+      pb[qt][0] = to_bf16x8(s[qt], 0);
+      pb[qt][1] = to_bf16x8(s[qt], 1);
+      dsb[qt][0] = to_bf16x8(dp[qt], 0);
+      dsb[qt][1] = to_bf16x8(dp[qt], 1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < C::T32; ++qt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 ga = read_tr8<C::CPR>(gs, qt * 32 + h2 * 16, dt * 32, lane);
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[qt][h2], adv[dt], 0, 0, 0);
+          const bf16x8 qa = read_tr8<C::CPR>(qs, qt * 32 + h2 * 16, dt * 32, lane);
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb[qt][h2], adk[dt], 0, 0, 0);
+        }
+  };
+
+  for (int it = 0; it < n_e; it += 2) {
+    do_block(q0s, g0s, q1s, g1s, it);
+    if (it + 1 < n_e) do_block(q1s, g1s, q0s, g0s, it + 1);
+  }
+
+  if (kk < N) {
+    __bf16* krow = dk + ((size_t)bh * N + kk) * D;
+    __bf16* vrow = dv + ((size_t)bh * N + kk) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ok, ov;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          ok[r4] = (__bf16)(adk[dt][g * 4 + r4] * scale);
+          ov[r4] = (__bf16)adv[dt][g * 4 + r4];
+        }
+        *reinterpret_cast<bf16x4*>(krow + dt * 32 + 8 * g + 4 * hf) = ok;
+        *reinterpret_cast<bf16x4*>(vrow + dt * 32 + 8 * g + 4 * hf) = ov;
+      }
+  }
+}
+
+template <int BS, int D>
+hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
+                           float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, const BackwardWs& w,
+                           hipStream_t s) {
+  dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
+      static_cast<__bf16*>(dq), p.N, p.nb, scale);
+  dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
+      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes) {
+  Carver c(ws);
+  BackwardWs w{};
+  const size_t padded = (size_t)p.B * p.H * p.nb * p.bs;
+  w.delta = c.take<float>(padded);
+  w.lse2 = c.take<float>(padded);
+  w.csc_start = c.take<int32_t>((size_t)p.R);
+  w.csc_count = c.take<int32_t>((size_t)p.R);
+  w.csc_row = c.take<int32_t>((size_t)(capacity > 0 ? capacity : 1));
+  *bytes = align_up(c.off, 256);
+  return w;
+}
+
+hipError_t launch_backward_fp32(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
+                                float scale, const bsa_csr* mask, void* dq, void* dk, void* dv,
+                                const BackwardWs& w, hipStream_t s);
+
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, float scale, const bsa_csr* mask, void* dq, void* dk,
+                           void* dv, const BackwardWs& w, hipStream_t s) {
+  const int BH = p.B * p.H;
+  const int npad = p.nb * p.bs;
+  const long long rows = (long long)BH * npad;
+  const int lpr = p.D / 8;
+  const unsigned grid_d = (unsigned)((rows * lpr + 255) / 256);
+  const bool bf = p.dtype == BSA_BF16;
+  if (p.D == 64) {
+    if (bf) delta_kernel<__bf16, 64><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
+                                                            static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
+                                                            p.N, npad, BH);
+    else delta_kernel<float, 64><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o), static_cast<const float*>(d_o),
+                                                        lse, w.delta, w.lse2, p.N, npad, BH);
+  } else {
+    if (bf) delta_kernel<__bf16, 128><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
+                                                             static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
+                                                             p.N, npad, BH);
+    else delta_kernel<float, 128><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o),
+                                                         static_cast<const float*>(d_o), lse, w.delta, w.lse2, p.N,
+                                                         npad, BH);
+  }
+  csc_kernel<<<BH, 256, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start, w.csc_count,
+                                w.csc_row);
+  if (!bf) return launch_backward_fp32(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
+  if (p.bs == 128 && p.D == 128) return launch_bwd_bf16<128, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
+  if (p.bs == 128 && p.D == 64) return launch_bwd_bf16<128, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
+  if (p.bs == 64 && p.D == 128) return launch_bwd_bf16<64, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
+  return launch_bwd_bf16<64, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
 }
 
 }  // namespace bsa

@@ -47,8 +47,7 @@ hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float
 
 // ---- forward (forward_bf16.hip, forward_fp32.hip) ----
 struct ForwardWs {
-  void* vt;          // bf16 path: V transposed per block, [B*H, nb, D, bs] (keys permuted)
-  float* part;       // [capacity, 2, bs] per-entry partial log2-sum-exp (block mass)
+  float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)
 };
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes);
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
@@ -60,14 +59,11 @@ hipError_t launch_forward_fp32(const Problem& p, const void* q, const void* k, c
 
 // ---- backward (backward.hip) ----
 struct BackwardWs {
-  float* delta;        // [B*H*N] rowsum(dO * O)
-  int32_t* csc_ptr;    // [B*H*nb + 1] key-major transpose of the mask
+  float* delta;        // [B*H, nb*bs] rowsum(dO * O), 0 on padding rows
+  float* lse2;         // [B*H, nb*bs] LSE * log2(e), +inf on padding rows
+  int32_t* csc_start;  // [B*H*nb] first transposed entry of key-block column (bh, j)
+  int32_t* csc_count;  // [B*H*nb] query blocks in that column
   int32_t* csc_row;    // [capacity] query block of each transposed entry
-  int32_t* csc_cnt;    // [B*H*nb] fill counters
-  void* vt;            // bf16 path: V transposed per block (as the forward)
-  void* qt;            // bf16 path: Q transposed per block
-  void* dot;           // bf16 path: dO transposed per block
-  void* kt;            // bf16 path: K transposed per block
 };
 BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes);
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,

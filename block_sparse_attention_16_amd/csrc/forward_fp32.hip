@@ -73,7 +73,7 @@ __global__ void fwd32_kernel(const float* __restrict__ q, const float* __restric
         m = m_new;
       }
     }
-    if (part != nullptr && sl == 0) part[(size_t)e * 2 * bs + ql] = lb > 0.f ? m + logf(lb) : -INFINITY;
+    if (part != nullptr && sl == 0) part[(size_t)e * bs + ql] = lb > 0.f ? m + logf(lb) : -INFINITY;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lsev = l > 0.f ? m + logf(l) : -INFINITY;
@@ -89,7 +89,7 @@ __global__ void fwd32_kernel(const float* __restrict__ q, const float* __restric
     const int j = col_idx[e];
     float x = 0.f;
     if (j >= 0 && j < nb)
-      for (int t = tid; t < nq; t += nthreads) x += expf(part[(size_t)e * 2 * bs + t] - lse_s[t]);
+      for (int t = tid; t < nq; t += nthreads) x += expf(part[(size_t)e * bs + t] - lse_s[t]);
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     if ((tid & 63) == 0) red[tid >> 6] = x;
     __syncthreads();

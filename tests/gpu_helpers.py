@@ -79,6 +79,7 @@ def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass
             err["lse"] = max(err["lse"], float(np.abs(lg[fin] - lo_[fin]).max()))
         a, z = rp[r], min(rp[r + 1], ci.size)
         if mass_gpu is not None and z > a:
+            assert np.isfinite(mass_gpu[a:z]).all(), f"row {r}: non-finite block mass"
             err["mass"] = max(err["mass"], float(np.abs(mass_gpu[a:z] - Mo[a:z]).max()))
     return err
 

@@ -52,7 +52,7 @@ def test_workspace_sizes():
     R, D, nb = 2 * 16, 64, 16
     assert est >= 2 * R * D * 4 + R * 4 + R * 4
     fwd = L.bsa_workspace_size(ctypes.byref(s), 1, 100)
-    assert fwd >= 100 * 2 * 64 * 4 + R * nb * 64 * 64 * 2 // nb
+    assert fwd >= 100 * 64 * 4          # per-entry, per-query partial sums for the block mass
     assert L.bsa_workspace_size(ctypes.byref(_shape(D=96)), 0, 0) == 0
     assert L.bsa_workspace_size(ctypes.byref(s), 7, 0) == 0
 

@@ -46,7 +46,7 @@ def _run_step(bsa, w, x, top_p, candidate=None, cand_host=None):
     R = w.B * w.H * w.nb
     sel_rows = sample_rows(R, w.nb, SAMPLE, seed=w.cfg_id)
     err = compare_forward(x["q"], x["k"], x["v"], w.block, rp, ci, default_scale(w.D), sel_rows,
-                          to_host(o), to_host(lse), to_host(mass), "bf16")
+                          to_host(o), to_host(lse), to_host(mass[:ci.size]), "bf16")
     print(f"[{w.name}] forward errors on {len(sel_rows)} rows: {err}", flush=True)
     assert_forward_within(err, "bf16", w.name)
     return mask, (rp, ci)
