@@ -102,6 +102,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="cogvideox")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the timed region, run one plain device-to-device copy of BYTES bytes "
+                         "(reference point for HBM byte counters under rocprofv3 --pmc)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards over heads "
@@ -174,6 +177,14 @@ def main(argv=None) -> int:
     est_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _, _ in ev]))
     fwd_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2, _ in ev]))
     bwd_ms = float(np.mean([e2.elapsed_time(e3) for _, _, e2, e3 in ev])) if w.backward else None
+
+    if a.copy_calibration > 0:
+        src = torch.empty(a.copy_calibration // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     rp, ci = mask.to_host()
     nnz = int(rp[-1])

@@ -9,11 +9,12 @@
 // the CSR rows, dK/dV key-major over a transposed (CSC) copy of the mask.
 //
 // Kernels, in launch order:
-//   delta_kernel  delta = rowsum(dO * O) and lse2 = LSE * log2(e), padded per
-//                 head to nb*BS rows (padding: delta 0, lse2 +inf -> P = 0)
+//   delta_kernel  lse2 = LSE * log2(e), padded per head to nb*BS rows (padding
+//                 +inf -> P = 0); on the fp32 path also delta = rowsum(dO * O)
 //   csc_kernel    one workgroup per head: counting transpose of the mask, rows
 //                 visited in order so every column lists query blocks ascending
-//   dq_kernel     per query block: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+//   dq_kernel     per query block: S^T = K Q^T, dP^T = V dO^T; pass 1 gives
+//                 delta = sum_k P dP, pass 2 dQ^T += K^T dS^T
 //   dkv_kernel    per key block:   S = Q K^T,   dP = dO V^T,
 //                 dV^T += dO^T P,  dK^T += Q^T dS
 //
@@ -22,6 +23,8 @@
 // (two ds_read_b64_tr_b16), the 32x32 accumulator of a lane holding one
 // column and 16 rows {8a + 4h + r}, and the k-slot permutation that lets an
 // accumulator, rounded to bf16, feed the next MFMA as its B operand.
+#include <type_traits>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -114,14 +117,15 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const floatx16& a, int half) {
 template <class T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ delta,
-                                                    float* __restrict__ lse2, int N, int npad, int BH) {
+                                                    float* __restrict__ lse2, int N, int npad, int BH,
+                                                    int with_delta) {
   constexpr int LPR = D / 8;                       // lanes per row, 8 elements each
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int row = gid / LPR, part = gid % LPR;     // row over BH * npad
   if (row >= BH * npad) return;
   const int bh = row / npad, t = row % npad;
   float s = 0.f;
-  if (t < N) {
+  if (with_delta && t < N) {
     const size_t off = ((size_t)bh * N + t) * D + part * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += (float)o[off + e] * (float)dout[off + e];
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
   if (part == 0) {
-    delta[row] = s;
+    if (with_delta) delta[row] = s;
     lse2[row] = t < N ? lse[(size_t)bh * N + t] * kLog2e : INFINITY;
   }
 }
@@ -198,13 +202,16 @@ __global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ ro
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query block (mask row).  Wave w owns queries
 // [32w, 32w+32); per visited key block j (tiles K_j, V_j in LDS):
-//   S^T = K Q^T, P^T = exp2(c2 S^T - lse2_q), dP^T = V dO^T,
-//   dS^T = P^T (dP^T - delta_q), dQ^T += K^T dS^T.
+//   S^T = K Q^T, P^T = exp2(c2 S^T - lse2_q), dP^T = V dO^T.
+// Pass 1 accumulates delta_q = sum_k P dP over the row in fp32 (equal to
+// dO_q . O_q for the exact O, without the rounding of a bf16 O) and stores it
+// for the dK/dV kernel; pass 2 forms dS^T = P^T (dP^T - delta_q) and
+// dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int BS, int D>
 __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
+    const __bf16* __restrict__ dout, float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
     __bf16* __restrict__ dq, int N, int nb, float scale) {
   using C = BCfg<BS, D>;
@@ -238,8 +245,8 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
   }
   const size_t prow = (size_t)bh * nb * BS + (size_t)i * BS + qloc;   // padded per-head row
   const float my_lse2 = lse2[prow];     // +inf for padding queries -> P = 0
-  const float my_delta = delta[prow];
   const float c2 = scale * kLog2e;
+  float my_delta = 0.f;
 
   floatx16 acc[C::DT];
 #pragma unroll
@@ -247,64 +254,75 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
-  if (n_e > 0) {
-    const int j0 = col_idx[e_begin];
-    dma_tiles<BS, D>(kh, vh, ((j0 >= 0 && j0 < nb) ? j0 : 0) * BS, N, k0s, v0s, wave, lane);
-  }
+  auto prologue = [&]() {
+    if (n_e > 0) {
+      const int j0 = col_idx[e_begin];
+      dma_tiles<BS, D>(kh, vh, ((j0 >= 0 && j0 < nb) ? j0 : 0) * BS, N, k0s, v0s, wave, lane);
+    }
+  };
 
-  auto do_block = [&](const char* ks, const char* vs, char* kn, char* vn, int it) __attribute__((always_inline)) {
+  // SECOND = false: accumulate sum_k P dP into dsum; true: dS and dQ.
+  auto do_block = [&](auto second, const char* ks, const char* vs, char* kn, char* vn, int it, float& dsum)
+                      __attribute__((always_inline)) {
     const int64_t e = e_begin + it;
     const int j_raw = col_idx[e];
     const bool valid = j_raw >= 0 && j_raw < nb;
     const int j = valid ? j_raw : 0;
+    const int nvk = valid ? min(BS, N - j * BS) : 0;   // valid keys in this block
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     if (it + 1 < n_e) {
       const int jn = col_idx[e + 1];
       dma_tiles<BS, D>(kh, vh, ((jn >= 0 && jn < nb) ? jn : 0) * BS, N, kn, vn, wave, lane);
     }
-    floatx16 st[C::T32], dpt[C::T32];
-#pragma unroll
-    for (int kt = 0; kt < C::T32; ++kt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) { st[kt][x] = 0.f; dpt[kt][x] = 0.f; }
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-#pragma unroll
-      for (int kt = 0; kt < C::T32; ++kt) {
-        const bf16x8 ka = read_row8<C::CPR>(ks, kt * 32 + l32, ds * 2 + hf);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ds], st[kt], 0, 0, 0);
-        const bf16x8 va = read_row8<C::CPR>(vs, kt * 32 + l32, ds * 2 + hf);
-        dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ds], dpt[kt], 0, 0, 0);
-      }
-    }
-    bf16x8 dsb[C::T32][2];
+    // one 32-key tile at a time keeps only two accumulators live
 #pragma unroll
     for (int kt = 0; kt < C::T32; ++kt) {
+      floatx16 st, dpt;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { st[x] = 0.f; dpt[x] = 0.f; }
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ++ds) {
+        const bf16x8 ka = read_row8<C::CPR>(ks, kt * 32 + l32, ds * 2 + hf);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ds], st, 0, 0, 0);
+        const bf16x8 va = read_row8<C::CPR>(vs, kt * 32 + l32, ds * 2 + hf);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ds], dpt, 0, 0, 0);
+      }
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int key = j * BS + kt * 32 + 8 * (x >> 2) + 4 * hf + (x & 3);
-        float p = __builtin_amdgcn_exp2f(fmaf(st[kt][x], c2, -my_lse2));
-        if (!valid || key >= N) p = 0.f;
-        st[kt][x] = p * (dpt[kt][x] - my_delta);
+        const int kl = kt * 32 + 8 * (x >> 2) + 4 * hf + (x & 3);
+        const float p = kl < nvk ? __builtin_amdgcn_exp2f(fmaf(st[x], c2, -my_lse2)) : 0.f;
+        if constexpr (decltype(second)::value) st[x] = p * (dpt[x] - my_delta);
+        else dsum = fmaf(p, dpt[x], dsum);
       }
-      dsb[kt][0] = to_bf16x8(st[kt], 0);
-      dsb[kt][1] = to_bf16x8(st[kt], 1);
-    }
+      if constexpr (decltype(second)::value) {
+        const bf16x8 ds0 = to_bf16x8(st, 0), ds1 = to_bf16x8(st, 1);
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int kt = 0; kt < C::T32; ++kt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 a = read_tr8<C::CPR>(ks, kt * 32 + h2 * 16, dt * 32, lane);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[kt][h2], acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 a0 = read_tr8<C::CPR>(ks, kt * 32, dt * 32, lane);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, ds0, acc[dt], 0, 0, 0);
+          const bf16x8 a1 = read_tr8<C::CPR>(ks, kt * 32 + 16, dt * 32, lane);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, ds1, acc[dt], 0, 0, 0);
         }
+      }
+    }
   };
 
+  using first_t = std::integral_constant<bool, false>;
+  using second_t = std::integral_constant<bool, true>;
+  float dsum = 0.f;
+  prologue();
   for (int it = 0; it < n_e; it += 2) {
-    do_block(k0s, v0s, k1s, v1s, it);
-    if (it + 1 < n_e) do_block(k1s, v1s, k0s, v0s, it + 1);
+    do_block(first_t{}, k0s, v0s, k1s, v1s, it, dsum);
+    if (it + 1 < n_e) do_block(first_t{}, k1s, v1s, k0s, v0s, it + 1, dsum);
+  }
+  my_delta = dsum + __shfl_xor(dsum, 32);
+  if (hf == 0) delta[prow] = my_delta;
+  __syncthreads();                      // every wave is done with the stage tiles
+  prologue();
+  for (int it = 0; it < n_e; it += 2) {
+    do_block(second_t{}, k0s, v0s, k1s, v1s, it, dsum);
+    if (it + 1 < n_e) do_block(second_t{}, k1s, v1s, k0s, v0s, it + 1, dsum);
   }
 
   if (qq < N) {
@@ -390,25 +408,20 @@ __global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
       const int in = qblock(it + 1);
       dma_tiles<BS, D>(qh, gh, (in < 0 ? 0 : in) * BS, N, qn, gn, wave, lane);
     }
-    // S and dP for every 32-query tile: lane holds key column kloc, query rows
-    floatx16 s[C::T32], dp[C::T32];
-#pragma unroll
-    for (int qt = 0; qt < C::T32; ++qt)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) { s[qt][x] = 0.f; dp[qt][x] = 0.f; }
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-#pragma unroll
-      for (int qt = 0; qt < C::T32; ++qt) {
-        const bf16x8 qa = read_row8<C::CPR>(qs, qt * 32 + l32, ds * 2 + hf);
-        s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s[qt], 0, 0, 0);
-        const bf16x8 ga = read_row8<C::CPR>(gs, qt * 32 + l32, ds * 2 + hf);
-        dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ds], dp[qt], 0, 0, 0);
-      }
-    }
-    bf16x8 pb[C::T32][2], dsb[C::T32][2];
+    // S and dP, one 32-query tile at a time: lane holds key column kloc and
+    // query rows {8a + 4h + r}
 #pragma unroll
     for (int qt = 0; qt < C::T32; ++qt) {
+      floatx16 s, dp;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
+#pragma unroll
+      for (int ds = 0; ds < C::DS; ++ds) {
+        const bf16x8 qa = read_row8<C::CPR>(qs, qt * 32 + l32, ds * 2 + hf);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
+        const bf16x8 ga = read_row8<C::CPR>(gs, qt * 32 + l32, ds * 2 + hf);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ds], dp, 0, 0, 0);
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qr = i * BS + qt * 32 + 8 * g + 4 * hf;       // 4 consecutive query rows
@@ -419,28 +432,25 @@ __global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int x = g * 4 + r4;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[qt][x], c2, -lv[r4]));
-          if (!valid) p = 0.f;
-          s[qt][x] = p;
-          dp[qt][x] = p * (dp[qt][x] - dv4[r4]);
+          const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[x], c2, -lv[r4])) : 0.f;
+          s[x] = p;
+          dp[x] = p * (dp[x] - dv4[r4]);
         }
       }
-      pb[qt][0] = to_bf16x8(s[qt], 0);
-      pb[qt][1] = to_bf16x8(s[qt], 1);
-      dsb[qt][0] = to_bf16x8(dp[qt], 0);
-      dsb[qt][1] = to_bf16x8(dp[qt], 1);
+      const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 1);
+      const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 1);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        bf16x8 a = read_tr8<C::CPR>(gs, qt * 32, dt * 32, lane);
+        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, adv[dt], 0, 0, 0);
+        a = read_tr8<C::CPR>(gs, qt * 32 + 16, dt * 32, lane);
+        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, adv[dt], 0, 0, 0);
+        a = read_tr8<C::CPR>(qs, qt * 32, dt * 32, lane);
+        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, d0, adk[dt], 0, 0, 0);
+        a = read_tr8<C::CPR>(qs, qt * 32 + 16, dt * 32, lane);
+        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, d1, adk[dt], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int qt = 0; qt < C::T32; ++qt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 ga = read_tr8<C::CPR>(gs, qt * 32 + h2 * 16, dt * 32, lane);
-          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb[qt][h2], adv[dt], 0, 0, 0);
-          const bf16x8 qa = read_tr8<C::CPR>(qs, qt * 32 + h2 * 16, dt * 32, lane);
-          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb[qt][h2], adk[dt], 0, 0, 0);
-        }
   };
 
   for (int it = 0; it < n_e; it += 2) {
@@ -474,7 +484,7 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
-      static_cast<__bf16*>(dq), p.N, p.nb, scale);
+      static_cast<__bf16*>(dq), p.N, p.nb, scale);   // also writes delta
   dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
@@ -513,16 +523,16 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   if (p.D == 64) {
     if (bf) delta_kernel<__bf16, 64><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
                                                             static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
-                                                            p.N, npad, BH);
+                                                            p.N, npad, BH, 0);
     else delta_kernel<float, 64><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o), static_cast<const float*>(d_o),
-                                                        lse, w.delta, w.lse2, p.N, npad, BH);
+                                                        lse, w.delta, w.lse2, p.N, npad, BH, 1);
   } else {
     if (bf) delta_kernel<__bf16, 128><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
                                                              static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
-                                                             p.N, npad, BH);
+                                                             p.N, npad, BH, 0);
     else delta_kernel<float, 128><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o),
                                                          static_cast<const float*>(d_o), lse, w.delta, w.lse2, p.N,
-                                                         npad, BH);
+                                                         npad, BH, 1);
   }
   csc_kernel<<<BH, 256, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start, w.csc_count,
                                 w.csc_row);

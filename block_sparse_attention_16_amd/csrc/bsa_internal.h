@@ -38,6 +38,7 @@ struct EstimateWs {
   float* kbar;       // [R, D] pooled key means
   int32_t* counts;   // [R] selected blocks per row
   uint32_t* bits;    // [R, words] selection bitmask
+  float* logits;     // [R, nb] pooled logits
   int words;         // ceil(nb / 32)
 };
 EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes);

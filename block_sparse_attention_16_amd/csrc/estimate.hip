@@ -8,9 +8,12 @@
 //
 // Kernels, in launch order:
 //   pool_kernel     HBM-streaming mean of Q and K over every token block
-//   select_kernel   one row per workgroup: pooled logits over the candidates,
-//                   LDS bitonic sort by (logit desc, id asc), fp32 softmax,
-//                   prefix sum, Top-p cut, forced prefix blocks -> bitmask
+//   logits_kernel   pooled logits scale * Qbar Kbar^T per head, a register-
+//                   tiled fp32 GEMM (each Kbar row is reused by 64 query rows)
+//   select_kernel   one wavefront per row: softmax over the row's candidates,
+//                   Top-p cut found by bisection on the ordered logit bits
+//                   (no sort), ties at the cut broken by lower block id,
+//                   forced prefix blocks -> selection bitmask
 //   scan_kernel     exclusive scan of the per-row counts -> CSR row_ptr
 //   compact_kernel  one wavefront per row: bitmask -> ascending col_idx
 #include "bsa_internal.h"
@@ -90,26 +93,86 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// One mask row per workgroup.  Produces counts[r] and the selection bitmask.
+// Pooled logits L[bh, i, j] = scale * <Qbar_i, Kbar_j> for one 64 x 64 tile
+// of one head; 256 threads, each a 4 x 4 block of outputs, d summed in order.
+// grid (ceil(nb/64), ceil(nb/64), B*H).
 template <int D>
+__global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restrict__ qbar,
+                                                          const float* __restrict__ kbar,
+                                                          float* __restrict__ logits, int nb, float scale) {
+  constexpr int DC = 32;                  // d chunk staged in LDS
+  __shared__ __attribute__((aligned(16))) float qs[DC][68];
+  __shared__ __attribute__((aligned(16))) float ks[DC][68];
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* qh = qbar + (size_t)bh * nb * D;
+  const float* kh = kbar + (size_t)bh * nb * D;
+  float acc[4][4] = {};
+  for (int d0 = 0; d0 < D; d0 += DC) {
+    // stage 64 rows x 32 dims of Qbar and Kbar, transposed to [d][row]
+    for (int x = tid; x < 64 * DC; x += kThreads) {
+      const int row = x / DC, d = x % DC;
+      qs[d][row] = i0 + row < nb ? qh[(size_t)(i0 + row) * D + d0 + d] : 0.f;
+      ks[d][row] = j0 + row < nb ? kh[(size_t)(j0 + row) * D + d0 + d] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int d = 0; d < DC; ++d) {
+      const float4 a = *reinterpret_cast<const float4*>(&qs[d][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&ks[d][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(av[u], bv[w], acc[u][w]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i0 + ty * 4 + u;
+    if (i >= nb) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = j0 + tx * 4 + w;
+      if (j < nb) logits[((size_t)bh * nb + i) * nb + j] = acc[u][w] * scale;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// One mask row per wavefront (4 rows per workgroup).  Lane l holds candidate
+// positions t = e*64 + l, e < EPL.  Top-p: with e_j = exp(s_j - max) and
+// M(T) = sum of e_j over ordered(s_j) >= T, the cut logit L* is the largest T
+// with M(T) >= p * Z, found bit by bit from the top; every block above L* is
+// kept and blocks exactly at L* are added in ascending id until the mass
+// reaches p * Z.  This is the shortest prefix of the (logit desc, id asc)
+// ranking whose cumulative probability reaches p, summed in another order.
+template <int EPL>
 __global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int nb, float top_p, float scale,
-    const int32_t* __restrict__ cand_ptr, const int32_t* __restrict__ cand_idx, int64_t cand_cap,
-    int n_forced, int32_t* __restrict__ counts, uint32_t* __restrict__ bits, int words) {
-  __shared__ unsigned long long key[kSortMax];
-  __shared__ float pre[kSortMax];
-  __shared__ float qrow[D];
-  __shared__ float wsum[kThreads / 64];
-  __shared__ float tsum[kThreads];
-  __shared__ uint32_t sel[kSortMax / 32];
-  __shared__ int first_hit;
-  __shared__ int nvalid_s;
+    const float* __restrict__ logits, int nb, int R, float top_p, const int32_t* __restrict__ cand_ptr,
+    const int32_t* __restrict__ cand_idx, int64_t cand_cap, int n_forced, int32_t* __restrict__ counts,
+    uint32_t* __restrict__ bits, int words) {
+  __shared__ uint32_t sel[kThreads / 64][kSortMax / 32];
+  __shared__ uint32_t seen[kThreads / 64][kSortMax / 32];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kThreads / 64) + wid;
+  if (r >= R) return;                        // whole wavefront leaves together
+  uint32_t* my_sel = sel[wid];
+  uint32_t* my_seen = seen[wid];
+  for (int w = lane; w < words; w += 64) { my_sel[w] = 0u; my_seen[w] = 0u; }
+  __builtin_amdgcn_wave_barrier();
 
-  const int r = blockIdx.x;
-  const int bh = r / nb;
-  const int tid = threadIdx.x;
-
-  // candidate range
   int n_c;
   int64_t lo = 0;
   if (cand_ptr) {
@@ -118,120 +181,113 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     if (a < 0) a = 0;
     if (a > b) a = b;
     lo = a;
-    n_c = (int)min<int64_t>(b - a, kSortMax);
+    n_c = (int)min<int64_t>(b - a, (int64_t)EPL * 64);
   } else {
     n_c = nb;
   }
-  int n_pow2 = 1;
-  while (n_pow2 < n_c) n_pow2 <<= 1;
-
-  if (tid < D) qrow[tid] = qbar[(size_t)r * D + tid];
-  if (tid == 0) { first_hit = 0x7fffffff; nvalid_s = 0; }
-  for (int w = tid; w < words; w += kThreads) sel[w] = 0u;
-  __syncthreads();
-
-  // pooled logits -> 64-bit sort keys (ordered logit bits << 32 | ~id); 0 = absent
-  for (int t = tid; t < n_pow2; t += kThreads) {
-    unsigned long long kk = 0ull;
+  const float* lrow = logits + (size_t)r * nb;
+  uint32_t key[EPL];
+  int jj[EPL];
+  float sv[EPL];
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int t = e * 64 + lane;
+    key[e] = 0u;                             // 0 = absent (finite logits order above 0)
+    jj[e] = -1;
+    sv[e] = 0.f;
     if (t < n_c) {
-      int j = cand_ptr ? cand_idx[lo + t] : t;
+      const int j = cand_ptr ? cand_idx[lo + t] : t;
       if (j >= 0 && j < nb) {
-        const float4* kr = reinterpret_cast<const float4*>(kbar + ((size_t)bh * nb + j) * D);
-        float acc = 0.f;
-#pragma unroll 8
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-          float4 v = kr[d4];
-          acc = fmaf(qrow[4 * d4 + 0], v.x, acc);
-          acc = fmaf(qrow[4 * d4 + 1], v.y, acc);
-          acc = fmaf(qrow[4 * d4 + 2], v.z, acc);
-          acc = fmaf(qrow[4 * d4 + 3], v.w, acc);
+        bool fresh = true;
+        if (cand_ptr) fresh = (atomicOr(&my_seen[j >> 5], 1u << (j & 31)) & (1u << (j & 31))) == 0u;
+        if (fresh) {
+          sv[e] = lrow[j];
+          key[e] = ordered_bits(sv[e]);
+          jj[e] = j;
+          kmax = max(kmax, key[e]);
         }
-        const float s = acc * scale;
-        kk = ((unsigned long long)ordered_bits(s) << 32) | (unsigned long long)(~(uint32_t)j);
       }
     }
-    key[t] = kk;
   }
-  __syncthreads();
-
-  // bitonic sort, descending
-  for (int kk = 2; kk <= n_pow2; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < (n_pow2 >> 1); t += kThreads) {
-        const int a = (t / j) * 2 * j + (t % j);
-        const int b = a + j;
-        const unsigned long long x = key[a], y = key[b];
-        const bool desc = (a & kk) == 0;
-        if (desc ? (x < y) : (x > y)) { key[a] = y; key[b] = x; }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  const float smax = kmax ? unordered_bits(kmax) : 0.f;
+  float ev[EPL];
+  float zl = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    ev[e] = key[e] ? expf(sv[e] - smax) : 0.f;
+    zl += ev[e];
+  }
+  const float Z = wave_sum(zl);
+  uint32_t cut = 1u;                         // keep every present block by default
+  bool tie_walk = false;
+  if (top_p < 1.0f && kmax != 0u) {
+    const float thr = top_p * Z;
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m += key[e] >= c ? ev[e] : 0.f;
+      if (wave_sum(m) >= thr) T = c;
+    }
+    cut = T;                                 // L*: M(L*) >= p Z > M(L* + 1)
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) nt += key[e] == T ? 1 : 0;
+    tie_walk = wave_sum_i(nt) > 1;
+    if (tie_walk) {
+      // several blocks share the cut logit: add them in ascending id
+      float mg = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) mg += key[e] > T ? ev[e] : 0.f;
+      const float m_gt = wave_sum(mg);
+      float etie = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) if (key[e] == T) etie = ev[e];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) etie = fmaxf(etie, __shfl_xor(etie, off));
+      // mark the tied ids, then one lane walks them in ascending order
+      for (int w = lane; w < words; w += 64) my_seen[w] = 0u;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        if (key[e] == T) atomicOr(&my_seen[jj[e] >> 5], 1u << (jj[e] & 31));
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) {
+        float acc = m_gt;
+        bool done = false;
+        for (int w = 0; w < words && !done; ++w) {
+          uint32_t b = my_seen[w];
+          while (b && !done) {
+            const int bit = __ffs(b) - 1;
+            b &= b - 1;
+            my_sel[w] |= 1u << bit;
+            acc += etie;
+            done = acc >= thr;
+          }
+        }
       }
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
     }
   }
-
-  // exp of (logit - max) for valid, non-duplicate entries; per-thread chunk prefix sums
-  const float smax = unordered_bits((uint32_t)(key[0] >> 32));
-  const int chunk = n_pow2 >= kThreads ? n_pow2 / kThreads : 1;
-  const int c0 = tid * chunk;
-  float run = 0.f;
-  int nv_local = 0;
-  for (int t = c0; t < c0 + chunk && t < n_pow2; ++t) {
-    const unsigned long long kv = key[t];
-    float e = 0.f;
-    if (kv != 0ull) {
-      ++nv_local;
-      const bool dup = t > 0 && key[t - 1] == kv;
-      if (!dup) e = expf(unordered_bits((uint32_t)(kv >> 32)) - smax);
-    }
-    run += e;
-    pre[t] = run;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const bool take = key[e] != 0u && (tie_walk ? key[e] > cut : key[e] >= cut);
+    if (take) atomicOr(&my_sel[jj[e] >> 5], 1u << (jj[e] & 31));
   }
-  tsum[tid] = run;
-  if (nv_local) atomicAdd(&nvalid_s, nv_local);
-  __syncthreads();
-  // inclusive scan of the per-thread totals (Hillis-Steele)
-  for (int off = 1; off < kThreads; off <<= 1) {
-    float v = tid >= off ? tsum[tid - off] : 0.f;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
-  }
-  const float offset = tid > 0 ? tsum[tid - 1] : 0.f;
-  const float total = tsum[kThreads - 1];
-  const int nvalid = nvalid_s;
-  const bool take_all = !(top_p < 1.0f);
-  const float thr = top_p * total;
-  for (int t = c0; t < c0 + chunk && t < nvalid; ++t) {
-    pre[t] += offset;
-    if (!take_all && pre[t] >= thr) { atomicMin(&first_hit, t); break; }
-  }
-  __syncthreads();
-  const int last = take_all ? nvalid - 1 : min(first_hit, nvalid - 1);
-  for (int t = tid; t <= last; t += kThreads) {
-    const unsigned long long kv = key[t];
-    const bool dup = t > 0 && key[t - 1] == kv;
-    if (!dup) {
-      const int j = (int)(~(uint32_t)(kv & 0xffffffffull));
-      atomicOr(&sel[j >> 5], 1u << (j & 31));
-    }
-  }
-  for (int j = tid; j < n_forced; j += kThreads) atomicOr(&sel[j >> 5], 1u << (j & 31));
-  __syncthreads();
-
+  for (int j = lane; j < n_forced; j += 64) atomicOr(&my_sel[j >> 5], 1u << (j & 31));
+  __builtin_amdgcn_wave_barrier();
   int cnt = 0;
-  for (int w = tid; w < words; w += kThreads) {
-    const uint32_t b = sel[w];
-    bits[(size_t)r * words + w] = b;
-    cnt += __popc(b);
+  for (int w = lane; w < words; w += 64) {
+    const uint32_t bw = my_sel[w];
+    bits[(size_t)r * words + w] = bw;
+    cnt += __popc(bw);
   }
-  // block reduction of the count
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if ((tid & 63) == 0) wsum[tid >> 6] = __int_as_float(cnt);
-  __syncthreads();
-  if (tid == 0) {
-    int tot = 0;
-    for (int w = 0; w < kThreads / 64; ++w) tot += __float_as_int(wsum[w]);
-    counts[r] = tot;
-  }
+  cnt = wave_sum_i(cnt);
+  if (lane == 0) counts[r] = cnt;
 }
 
 // Exclusive scan of counts[R] into row_ptr[R+1]; a single workgroup of 1024 threads.
@@ -303,18 +359,26 @@ EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes) {
   w.kbar = c.take<float>((size_t)p.R * p.D);
   w.counts = c.take<int32_t>((size_t)p.R);
   w.bits = c.take<uint32_t>((size_t)p.R * w.words);
+  w.logits = c.take<float>((size_t)p.R * p.nb);
   *bytes = align_up(c.off, 256);
   return w;
 }
 
 template <class T, int D>
-static void launch_pool_select(const Problem& p, const void* q, const void* k, float top_p, float scale,
-                               const bsa_csr* cand, int n_forced, const EstimateWs& w, hipStream_t s) {
+static void launch_pool_logits(const Problem& p, const void* q, const void* k, float scale, const EstimateWs& w,
+                               hipStream_t s) {
   pool_kernel<T, D><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar, w.kbar,
                                              p.N, p.bs, p.nb);
-  select_kernel<D><<<p.R, kThreads, 0, s>>>(w.qbar, w.kbar, p.nb, top_p, scale, cand ? cand->row_ptr : nullptr,
-                                            cand ? cand->col_idx : nullptr, cand ? cand->capacity : 0, n_forced,
-                                            w.counts, w.bits, w.words);
+  const dim3 g((p.nb + 63) / 64, (p.nb + 63) / 64, p.B * p.H);
+  logits_kernel<D><<<g, kThreads, 0, s>>>(w.qbar, w.kbar, w.logits, p.nb, scale);
+}
+
+template <int EPL>
+static void launch_select(const Problem& p, float top_p, const bsa_csr* cand, int n_forced, const EstimateWs& w,
+                          hipStream_t s) {
+  select_kernel<EPL><<<(p.R + 3) / 4, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, cand ? cand->row_ptr : nullptr,
+                                                        cand ? cand->col_idx : nullptr, cand ? cand->capacity : 0,
+                                                        n_forced, w.counts, w.bits, w.words);
 }
 
 hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
@@ -323,12 +387,16 @@ hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float
   const int n_forced = min(p.nb, (keep_prefix_tokens + p.bs - 1) / p.bs);
   const bool bf = p.dtype == BSA_BF16;
   if (p.D == 64) {
-    if (bf) launch_pool_select<__bf16, 64>(p, q, k, top_p, scale, cand, n_forced, w, s);
-    else launch_pool_select<float, 64>(p, q, k, top_p, scale, cand, n_forced, w, s);
+    if (bf) launch_pool_logits<__bf16, 64>(p, q, k, scale, w, s);
+    else launch_pool_logits<float, 64>(p, q, k, scale, w, s);
   } else {
-    if (bf) launch_pool_select<__bf16, 128>(p, q, k, top_p, scale, cand, n_forced, w, s);
-    else launch_pool_select<float, 128>(p, q, k, top_p, scale, cand, n_forced, w, s);
+    if (bf) launch_pool_logits<__bf16, 128>(p, q, k, scale, w, s);
+    else launch_pool_logits<float, 128>(p, q, k, scale, w, s);
   }
+  if (p.nb <= 64) launch_select<1>(p, top_p, cand, n_forced, w, s);
+  else if (p.nb <= 256) launch_select<4>(p, top_p, cand, n_forced, w, s);
+  else if (p.nb <= 1024) launch_select<16>(p, top_p, cand, n_forced, w, s);
+  else launch_select<64>(p, top_p, cand, n_forced, w, s);
   scan_kernel<<<1, 1024, 0, s>>>(w.counts, out->row_ptr, p.R);
   compact_kernel<<<(p.R + 3) / 4, kThreads, 0, s>>>(w.bits, out->row_ptr, out->col_idx, out->capacity, p.R,
                                                     w.words);

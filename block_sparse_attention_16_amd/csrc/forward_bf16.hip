@@ -8,7 +8,8 @@
 //
 // Workgroup = one mask row (query block i of head bh), BS/32 waves.  Wave w
 // owns queries [32w, 32w + 32) of the block and every key of each visited key
-// block, with its own online-softmax state.
+// block, with its own online-softmax state.  Two workgroups share a CU so that
+// one's softmax (VALU) overlaps the other's matrix work.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = K rows from LDS, B = Q^T held in registers.  In the 32x32 accumulator a
@@ -20,9 +21,11 @@
 // 4x4 blocks of bf16 across each 16-lane group.
 //
 // K and V tiles stream from HBM/L2 straight into LDS with
-// global_load_lds_dwordx4, double-buffered: block t+1 is in flight while
-// block t is computed.  LDS rows are XOR-swizzled in 16-byte chunks so the
-// MFMA operand reads are bank-conflict free.
+// global_load_lds_dwordx4.  D = 64: two stages (double buffer).  D = 128: one
+// K tile and one V tile (64 KB, so two workgroups fit a CU); the DMA of the
+// next K tile overlaps this block's softmax and PV, the next V tile overlaps
+// the next block's scores.  LDS rows are XOR-swizzled in 16-byte chunks so
+// the MFMA operand reads are bank-conflict free.
 //
 // Block mass: for every visited entry e and query q the kernel stores the
 // block-local log2-sum-exp m + log2(l_block) (exact whatever the running max
@@ -40,6 +43,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;     // lazy-rescale threshold of the running max, log2 units
 
 // 16-byte chunk swizzles of a [key][D] bf16 tile whose rows are CPR chunks long.
 // K is read with ds_read_b128 down 16 consecutive rows; V with ds_read_b64_tr_b16
@@ -69,47 +73,160 @@ template <int BS, int D>
 struct Cfg {
   static constexpr int NW = BS / 32;                  // waves; wave w owns 32 queries
   static constexpr int THREADS = NW * 64;
-  static constexpr int KT = BS / 32;                  // 32-key tiles per block
+  static constexpr int WG_PER_CU = 8 / NW;            // two waves per SIMD
+  // Key blocks stream through LDS in sub-blocks of SUB keys, double-buffered;
+  // each sub-block is scored and folded into the softmax in chunks of KC
+  // 32-key tiles (KC*16 score registers per lane).
+  static constexpr int SUB = D == 64 ? BS : (BS == 128 ? 64 : 32);
+  static constexpr int U = BS / SUB;                  // sub-blocks per key block
+  static constexpr int KU = SUB / 32;                 // 32-key tiles per sub-block
+  static constexpr int KC = KU < 2 ? KU : 2;          // tiles per softmax chunk
   static constexpr int DS = D / 16, DT = D / 32;      // MFMA k-steps over d, d tiles
   static constexpr int CPR = D / 8;                   // 16-byte chunks per K or V row
-  static constexpr int TILE_BYTES = BS * D * 2;       // one K or V tile
+  static constexpr int TILE_BYTES = SUB * D * 2;      // one K or V sub-tile
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);  // dma ops per thread per tile
   static_assert(LOADS * 16 * THREADS == TILE_BYTES, "tile must split evenly over the waves");
+  static_assert(4 * TILE_BYTES * WG_PER_CU <= 160 * 1024, "LDS of the resident workgroups");
 };
 
-// Issue the DMA of K block j and V block j into one LDS stage.  Lane l of a
-// wave writes LDS chunk (wave chunk base + l); the global source is the
-// logical chunk that the swizzle places there.  Keys past N repeat row N-1
-// (their scores are masked to -inf, so their V rows get weight 0).
-template <int BS, int D>
-__device__ __forceinline__ void issue_tile_loads(const __bf16* __restrict__ kh, const __bf16* __restrict__ vh,
-                                                 int j, int N, char* ktile, char* vtile, int wave, int lane) {
+// DMA of rows [key0, key0 + SUB) of a [N, D] bf16 matrix into a swizzled LDS
+// tile.  Lane l of a wave writes LDS chunk (wave chunk base + l); the global
+// source is the logical chunk the swizzle places there.  Keys past N repeat
+// row N-1 (their scores are masked to -inf, so their V rows get weight 0).
+template <int BS, int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(const __bf16* __restrict__ src, int key0, int N, char* tile, int wave,
+                                         int lane) {
   using C = Cfg<BS, D>;
-  const int key0 = j * BS;
 #pragma unroll
   for (int it = 0; it < C::LOADS; ++it) {
     const int chunk0 = (it * C::NW + wave) * 64;   // first LDS chunk of this wave's 1 KB
     const int L = chunk0 + lane;
     const int row = L / C::CPR, pos = L % C::CPR;
-    const size_t src = (size_t)min(key0 + row, N - 1) * D;
-    lds_dma16(kh + src + (pos ^ swz_k<C::CPR>(row)) * 8, ktile + chunk0 * 16);
-    lds_dma16(vh + src + (pos ^ swz_v<C::CPR>(row)) * 8, vtile + chunk0 * 16);
+    const int c = pos ^ (IS_V ? swz_v<C::CPR>(row) : swz_k<C::CPR>(row));
+    lds_dma16(src + (size_t)min(key0 + row, N - 1) * D + c * 8, tile + chunk0 * 16);
+  }
+}
+
+// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.
+template <int BS, int D, int NT, class C = Cfg<BS, D>>
+__device__ __forceinline__ void scores(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&st)[NT], int t0,
+                                       int l32, int hf) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) st[t][v2] = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int row = (t0 + t) * 32 + l32;
+      const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+      st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], st[t], 0, 0, 0);
+    }
+  }
+}
+
+// Online-softmax update and O^T += V^T P^T for the KC 32-key tiles t0 ..
+// t0 + KC - 1 of the sub-tile, whose scores are st[s0 ..].  nvk = valid keys
+// in the sub-tile (wave-uniform).
+template <int BS, int D, int NT, class C = Cfg<BS, D>>
+__device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, const char* vs, int nvk, float c2,
+                                           float& m_run, float& l_run, float& ls_blk, floatx16 (&acc)[C::DT],
+                                           int lane) {
+  const int hf = lane >> 5;
+  // mask keys past the end of the sequence (partial last block) or of an
+  // invalid entry: a select against the wave-uniform valid-key count
+  if (nvk < C::SUB) {
+#pragma unroll
+    for (int t = 0; t < C::KC; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) {
+        const int kl = (t0 + t) * 32 + 8 * (v2 >> 2) + 4 * hf + (v2 & 3);
+        st[s0 + t][v2] = kl < nvk ? st[s0 + t][v2] : -INFINITY;
+      }
+  }
+  // The running max is only raised when some lane's new max exceeds it by
+  // more than kTau (log2 units): p <= 2^kTau stays safe in bf16/fp32 and most
+  // updates skip the rescale of the output accumulators.  Exact for any m_run.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < C::KC; ++t)
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, st[s0 + t][v2]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+  if (__any(mx > m_run + kTau)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
+    l_run *= alpha;
+    ls_blk *= alpha;
+  }
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  bf16x8 pb[C::KC][2];
+  float ls = 0.f;
+#pragma unroll
+  for (int t = 0; t < C::KC; ++t) {
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(st[s0 + t][v2], c2, -m_use));
+      st[s0 + t][v2] = p;
+      ls += p;
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) pb[t][h2][e2] = (__bf16)st[s0 + t][h2 * 8 + e2];
+  }
+  ls += __shfl_xor(ls, 32);
+  l_run += ls;
+  ls_blk += ls;
+
+  // O^T += V^T P^T.  Source-lane role in the transposing read: lane
+  // 16G + 4t + g points at key row (.. + 8x + 4(G/2) + t), dims
+  // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
+  // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.
+  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
+#pragma unroll
+    for (int t = 0; t < C::KC; ++t) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        short4_t t4[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
+          const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
+          t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
+        }
+        // whole-register reinterpretation (element-wise casts of the
+        // transposed halves are mis-assembled by the compiler)
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][h2], acc[dt], 0, 0, 0);
+      }
+    }
   }
 }
 
 template <int BS, int D>
-__global__ __launch_bounds__(2 * BS, 1) void fwd_kernel(   // 2*BS = Cfg::THREADS
+__global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two waves per SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, int N, int nb, int R, float scale,
     int xcd_remap) {
   using C = Cfg<BS, D>;
-  // Two LDS stages, each a K tile and a V tile.  Four distinct objects, each
-  // used at a fixed place in the 2x-unrolled loop, let the compiler see that
-  // reads of one stage do not wait on the DMA into the other.
+  // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
+  // the compiler see that reads of one tile do not wait on the DMA into another.
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
   __shared__ float lse2_s[BS];
 
@@ -158,120 +275,52 @@ __global__ __launch_bounds__(2 * BS, 1) void fwd_kernel(   // 2*BS = Cfg::THREAD
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = scale * kLog2e;   // logits in base-2 units
 
-  if (n_e > 0) {
-    const int j0 = col_idx[e_begin];
-    issue_tile_loads<BS, D>(kh, vh, (j0 >= 0 && j0 < nb) ? j0 : 0, N, k0s, v0s, wave, lane);
-  }
-
-  // One visited key block: wait for its tiles, start the DMA of the next
-  // block into the other stage, then compute.
-  auto do_block = [&](const char* ks, const char* vs, char* kn, char* vn, int it) __attribute__((always_inline)) {
-    const int64_t e = e_begin + it;
-    const int j_raw = col_idx[e];
+  // Unit u = sub-block (u % U) of CSR entry (u / U).
+  const int n_u = n_e * C::U;
+  auto unit_src = [&](int u, int& nvk) {      // first key of the unit; nvk = its valid keys
+    const int j_raw = col_idx[e_begin + u / C::U];
     const bool valid = j_raw >= 0 && j_raw < nb;
-    const int j = valid ? j_raw : 0;
+    const int key0 = (valid ? j_raw : 0) * BS + (u % C::U) * C::SUB;
+    nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
+    return key0;
+  };
+  if (n_u > 0) {
+    int nv;
+    const int key0 = unit_src(0, nv);
+    dma_tile<BS, D, false>(kh, key0, N, k0s, wave, lane);
+    dma_tile<BS, D, true>(vh, key0, N, v0s, wave, lane);
+  }
+  float ls_blk = 0.f;      // current entry's sum of exp2(s - m_run), for the block mass
+
+  // One unit: wait for its tiles, start the DMA of the next unit into the
+  // other stage, then score and fold it into the softmax chunk by chunk.
+  auto do_unit = [&](const char* ks, const char* vs, char* kn, char* vn, int u) __attribute__((always_inline)) {
+    int nvk;
+    unit_src(u, nvk);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA into the current stage landed
     __syncthreads();                      // ... and every other wave's
-    if (it + 1 < n_e) {
-      const int jn = col_idx[e + 1];
-      issue_tile_loads<BS, D>(kh, vh, (jn >= 0 && jn < nb) ? jn : 0, N, kn, vn, wave, lane);
+    if (u + 1 < n_u) {
+      int nn;
+      const int key1 = unit_src(u + 1, nn);
+      dma_tile<BS, D, false>(kh, key1, N, kn, wave, lane);
+      dma_tile<BS, D, true>(vh, key1, N, vn, wave, lane);
     }
-
-    // S^T = K Q^T over the whole key block
-    floatx16 st[C::KT];
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) st[kt][v2] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt) {
-        const int row = kt * 32 + l32;
-        const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], st[kt], 0, 0, 0);
-      }
+    for (int c0 = 0; c0 < C::KU; c0 += C::KC) {
+      floatx16 sh[C::KC];
+      scores<BS, D, C::KC>(ks, qf, sh, c0, l32, hf);
+      softmax_pv<BS, D, C::KC>(sh, 0, c0, vs, nvk, c2, m_run, l_run, ls_blk, acc, lane);
     }
-
-    // mask keys past the end of the sequence (partial last block) or of an invalid entry
-    if (!valid || j * BS + BS > N) {
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-        for (int v2 = 0; v2 < 16; ++v2) {
-          const int key = j * BS + kt * 32 + 8 * (v2 >> 2) + 4 * hf + (v2 & 3);
-          if (!valid || key >= N) st[kt][v2] = -INFINITY;
-        }
-    }
-
-    // online softmax of this lane's query column
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, st[kt][v2]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    bf16x8 pb[C::KT][2];
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][v2], c2, -m_use));
-        st[kt][v2] = p;
-        ls += p;
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) pb[kt][h2][e2] = (__bf16)st[kt][h2 * 8 + e2];
-    }
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
-    if (part != nullptr && hf == 0)
-      part[e * BS + qloc] = ls > 0.f ? m_use + __builtin_amdgcn_logf(ls) : -INFINITY;
-
-    // O^T += V^T P^T.  Source-lane role in the transposing read: lane
-    // 16G + 4t + g points at key row (.. + 8x + 4(G/2) + t), dims
-    // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
-    // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.
-    const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          short4_t t4[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int row = kt * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
-            const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
-            t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
-          }
-          // whole-register reinterpretation (element-wise casts of the
-          // transposed halves are mis-assembled by the compiler)
-          const bf16x8 a =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][h2], acc[dt], 0, 0, 0);
-        }
-      }
+    if (u % C::U == C::U - 1) {         // last sub-block of the entry
+      const int it = u / C::U;
+      if (part != nullptr && hf == 0)
+        part[(e_begin + it) * BS + qloc] = ls_blk > 0.f ? m_run + __builtin_amdgcn_logf(ls_blk) : -INFINITY;
+      ls_blk = 0.f;
     }
   };
-
-  for (int it = 0; it < n_e; it += 2) {
-    do_block(k0s, v0s, k1s, v1s, it);
-    if (it + 1 < n_e) do_block(k1s, v1s, k0s, v0s, it + 1);
+  for (int u = 0; u < n_u; u += 2) {
+    do_unit(k0s, v0s, k1s, v1s, u);
+    if (u + 1 < n_u) do_unit(k1s, v1s, k0s, v0s, u + 1);
   }
 
   // ---- normalise, write O and LSE ----

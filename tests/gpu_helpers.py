@@ -98,3 +98,30 @@ def sample_rows(R: int, nb: int, count: int, seed: int = 0) -> list[int]:
     fixed = {0, nb - 1, R - nb, R - 1}
     extra = rng.choice(R, size=min(count, R), replace=False).tolist()
     return sorted(fixed | set(extra))
+
+
+def head_csr(rp, ci, H: int, nb: int, b: int, h: int):
+    """CSR rows of one head, rebased to start at 0."""
+    r0 = (b * H + h) * nb
+    sub_rp = rp[r0:r0 + nb + 1] - rp[r0]
+    sub_ci = ci[rp[r0]:rp[r0 + nb]]
+    return sub_rp, sub_ci
+
+
+def compare_backward(x, block, rp, ci, scale, heads, grads_gpu, dtype: str):
+    """Oracle gradients of sum(O * G) for the listed heads vs the GPU's; max errors."""
+    tol = TOL[dtype]
+    B, H, N, D = x["q"].shape
+    nb = O.num_blocks(N, block)
+    err = {"dq": 0.0, "dk": 0.0, "dv": 0.0, "excess": -1.0}
+    for b, h in heads:
+        srp, sci = head_csr(rp, ci, H, nb, b, h)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        dQ, dK, dV = O.sparse_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl], block, srp, sci, scale)
+        for name, want in (("dq", dQ), ("dk", dK), ("dv", dV)):
+            got = grads_gpu[name][b, h]
+            diff = np.abs(got - want[0, 0])
+            err[name] = max(err[name], float(diff.max()))
+            err["excess"] = max(err["excess"],
+                                float((diff - tol["grad"] - tol["store_rel"] * np.abs(want[0, 0])).max()))
+    return err

@@ -214,3 +214,46 @@ def test_host_validation_errors(bsa):
     with pytest.raises(bsa.BsaError) as e:
         bsa.bsa_estimate_mask(q, q, 0.5, 32)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D,bs", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("N", [37, 300])
+def test_backward_random_masks_ragged(bsa, dtype, D, bs, N):
+    from tests.gpu_helpers import compare_backward
+    rng = np.random.default_rng(7 * N + D + bs)
+    B, H = 1, 2
+    q, k, v = _inputs(rng, B, H, N, D, dtype, scale_q=0.5)
+    g = rng.normal(size=(B, H, N, D)).astype(np.float32)
+    if dtype == "bf16":
+        g = round_to_bf16(g)
+    nb = O.num_blocks(N, bs)
+    rows = []
+    for r in range(B * H * nb):
+        if r % 4 == 1:
+            rows.append(np.zeros(0, np.int64))
+        else:
+            rows.append(np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False)))
+    rp, ci = O.rows_to_csr(rows)
+    mask = bsa.csr_from_host(rp, ci, "cuda")
+    qd, kd, vd, gd = (to_device(t, dtype) for t in (q, k, v, g))
+    o, lse, _ = bsa.bsa_forward(qd, kd, vd, mask, bs, want_mass=False)
+    dq, dk, dv = bsa.bsa_backward(qd, kd, vd, o, gd, lse, mask, bs)
+    torch.cuda.synchronize()
+    x = {"q": q, "k": k, "v": v, "g": g}
+    err = compare_backward(x, bs, rp, ci, default_scale(D), [(0, 0), (0, 1)],
+                           {"dq": to_host(dq), "dk": to_host(dk), "dv": to_host(dv)}, dtype)
+    assert err["excess"] <= 0.0, f"gradient errors {err}"
+
+
+def test_backward_is_deterministic(bsa):
+    w = get("tiny")
+    x = make_inputs(w, dtype="bf16", want_grad=True)
+    q, k, v, g = (to_device(x[n], "bf16") for n in "qkvg")
+    m = bsa.bsa_estimate_mask(q, k, 0.9, w.block)
+    o, lse, _ = bsa.bsa_forward(q, k, v, m, w.block, want_mass=False)
+    a = bsa.bsa_backward(q, k, v, o, g, lse, m, w.block)
+    b = bsa.bsa_backward(q, k, v, o, g, lse, m, w.block)
+    torch.cuda.synchronize()
+    for t1, t2 in zip(a, b):
+        assert torch.equal(t1, t2)

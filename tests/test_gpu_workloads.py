@@ -75,7 +75,17 @@ def test_wan_reduced_search_steps(bsa):
                 assert set(ci[rp[r]:rp[r + 1]].tolist()) <= set(fci[frp[r]:frp[r + 1]].tolist())
 
 
-def test_dsv_training_forward(bsa):
+def test_dsv_training_forward_and_backward(bsa):
+    from tests.gpu_helpers import compare_backward
     w = get("dsv_train")
-    x = make_inputs(w, dtype="bf16", want_grad=False)
-    _run_step(bsa, w, x, f32(w.top_p[0]))
+    x = make_inputs(w, dtype="bf16", want_grad=True)
+    mask, (rp, ci) = _run_step(bsa, w, x, f32(w.top_p[0]))
+    q, k, v, g = (to_device(x[n], "bf16") for n in "qkvg")
+    o, lse, _ = bsa.bsa_forward(q, k, v, mask, w.block, want_mass=False)
+    dq, dk, dv = bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (1, w.H - 1)]
+    grads = {"dq": to_host(dq), "dk": to_host(dk), "dv": to_host(dv)}
+    err = compare_backward(x, w.block, rp, ci, default_scale(w.D), heads, grads, "bf16")
+    print(f"[{w.name}] gradient errors on heads {heads}: {err}", flush=True)
+    assert err["excess"] <= 0.0, f"gradient errors {err}"
