@@ -65,6 +65,19 @@ __device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
 }
 
+// Combine a value with its partner in the other half of the wave (lane ^ 32)
+// with v_permlane32_swap, a VALU op: swapping x with itself yields
+// [x_lo, x_lo] and [x_hi, x_hi], so op(r0, r1) = op(x[l%32], x[l%32 + 32]) on
+// every lane, identically on both halves.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
@@ -107,7 +120,8 @@ __device__ __forceinline__ void dma_tile(const __bf16* __restrict__ src, int key
   }
 }
 
-// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.
+// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.  The K operands
+// of step ds+1 are read while the MFMAs of step ds run.
 template <int BS, int D, int NT, class C = Cfg<BS, D>>
 __device__ __forceinline__ void scores(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&st)[NT], int t0,
                                        int l32, int hf) {
@@ -115,15 +129,24 @@ __device__ __forceinline__ void scores(const char* ks, const bf16x8 (&qf)[C::DS]
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) st[t][v2] = 0.f;
+  auto read_k = [&](int ds, int t) {
+    const int row = (t0 + t) * 32 + l32;
+    const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
+    return *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+  };
+  bf16x8 cur[NT], nxt[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cur[t] = read_k(0, t);
 #pragma unroll
   for (int ds = 0; ds < C::DS; ++ds) {
+    if (ds + 1 < C::DS) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int row = (t0 + t) * 32 + l32;
-      const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
-      st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], st[t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) nxt[t] = read_k(ds + 1, t);
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[t], qf[ds], st[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
   }
 }
 
@@ -154,7 +177,7 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, c
   for (int t = 0; t < C::KC; ++t)
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, st[s0 + t][v2]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+  mx = xhalf_max(mx) * c2;
   if (__any(mx > m_run + kTau)) {
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -182,7 +205,7 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, c
 #pragma unroll
       for (int e2 = 0; e2 < 8; ++e2) pb[t][h2][e2] = (__bf16)st[s0 + t][h2 * 8 + e2];
   }
-  ls += __shfl_xor(ls, 32);
+  ls = xhalf_sum(ls);
   l_run += ls;
   ls_blk += ls;
 
@@ -191,27 +214,28 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, c
   // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
   // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.
   const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+  auto read_v = [&](int step) {          // step = (dt * KC + t) * 2 + h2
+    const int h2 = step & 1, t = (step >> 1) % C::KC, dt = (step >> 1) / C::KC;
     const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
+    short4_t t4[2];
 #pragma unroll
-    for (int t = 0; t < C::KC; ++t) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        short4_t t4[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
-          const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
-          t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
-        }
-        // whole-register reinterpretation (element-wise casts of the
-        // transposed halves are mis-assembled by the compiler)
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][h2], acc[dt], 0, 0, 0);
-      }
+    for (int x = 0; x < 2; ++x) {
+      const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
+      const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
+      t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
     }
+    // whole-register reinterpretation (element-wise casts of the transposed
+    // halves are mis-assembled by the compiler)
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int NSTEP = C::DT * C::KC * 2;
+  bf16x8 cur = read_v(0);
+#pragma unroll
+  for (int step = 0; step < NSTEP; ++step) {
+    const bf16x8 nxt = step + 1 < NSTEP ? read_v(step + 1) : cur;     // read one step ahead
+    const int h2 = step & 1, t = (step >> 1) % C::KC, dt = (step >> 1) / C::KC;
+    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pb[t][h2], acc[dt], 0, 0, 0);
+    cur = nxt;
   }
 }
 
@@ -219,8 +243,7 @@ template <int BS, int D>
 __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two waves per SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, int N, int nb, int R, float scale,
-    int xcd_remap) {
+    float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, int N, int nb, float scale) {
   using C = Cfg<BS, D>;
   // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
   // the compiler see that reads of one tile do not wait on the DMA into another.
@@ -230,14 +253,10 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
   __shared__ float lse2_s[BS];
 
-  // blockIdx -> mask row.  Workgroups are dealt to the 8 XCDs round-robin;
-  // with xcd_remap each XCD takes a contiguous range of rows instead.
-  int r = blockIdx.x;
-  if (xcd_remap) {
-    const int per = (R + 7) / 8;
-    r = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (r >= R) return;
-  }
+  // blockIdx -> mask row, dealt to the 8 XCDs round-robin by the dispatcher
+  // (finer-grained than any contiguous split, which balances rows of unequal
+  // length; keeping neighbouring rows on one XCD's L2 measured no faster).
+  const int r = blockIdx.x;
   const int bh = r / nb, i = r - bh * nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -362,12 +381,9 @@ template <int BS, int D>
 hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const void* v, float scale,
                        const bsa_csr* mask, void* o, float* lse, float* mass, const ForwardWs& w, hipStream_t s) {
   using C = Cfg<BS, D>;
-  const int xcd = 0;
-  const int grid = xcd ? ((p.R + 7) / 8) * 8 : p.R;
-  fwd_kernel<BS, D><<<grid, C::THREADS, 0, s>>>(
+  fwd_kernel<BS, D><<<p.R, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
-      mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, p.N, p.nb, p.R,
-      scale, xcd);
+      mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, p.N, p.nb, scale);
   return hipGetLastError();
 }
 
