@@ -78,8 +78,19 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// Buffer resource over one head's [N, D] bf16 matrix: raw (stride 0), its
+// record count the matrix size in bytes, so that reads past the last key
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const __bf16* base, int N, int D) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), (short)0, N * D * 2, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset `off` into LDS at lds_wave_base + 16 * lane.
+// The buffer form (not global_load_lds) lets the compiler keep exact LDS
+// wait counts while the copy is in flight.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0,
+                                           0, 0);
 }
 
 template <int BS, int D>
@@ -102,52 +113,59 @@ struct Cfg {
   static_assert(4 * TILE_BYTES * WG_PER_CU <= 160 * 1024, "LDS of the resident workgroups");
 };
 
-// DMA of rows [key0, key0 + SUB) of a [N, D] bf16 matrix into a swizzled LDS
-// tile.  Lane l of a wave writes LDS chunk (wave chunk base + l); the global
-// source is the logical chunk the swizzle places there.  Keys past N repeat
-// row N-1 (their scores are masked to -inf, so their V rows get weight 0).
+// Per-lane byte offset, within a SUB-row window of a [N, D] bf16 matrix, of
+// the 16-byte source chunk that dma op `it` of this lane stores.  Lane l of a
+// wave writes LDS chunk (wave chunk base + l); the swizzle decides which
+// logical chunk lands there.
 template <int BS, int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const __bf16* __restrict__ src, int key0, int N, char* tile, int wave,
-                                         int lane) {
+__device__ __forceinline__ uint32_t dma_src_off(int it, int wave, int lane) {
   using C = Cfg<BS, D>;
-#pragma unroll
-  for (int it = 0; it < C::LOADS; ++it) {
-    const int chunk0 = (it * C::NW + wave) * 64;   // first LDS chunk of this wave's 1 KB
-    const int L = chunk0 + lane;
-    const int row = L / C::CPR, pos = L % C::CPR;
-    const int c = pos ^ (IS_V ? swz_v<C::CPR>(row) : swz_k<C::CPR>(row));
-    lds_dma16(src + (size_t)min(key0 + row, N - 1) * D + c * 8, tile + chunk0 * 16);
-  }
+  const int L = (it * C::NW + wave) * 64 + lane;
+  const int row = L / C::CPR, pos = L % C::CPR;
+  const int c = pos ^ (IS_V ? swz_v<C::CPR>(row) : swz_k<C::CPR>(row));
+  return (uint32_t)((row * D + c * 8) * 2);
 }
 
-// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.  The K operands
-// of step ds+1 are read while the MFMAs of step ds run.
+// DMA of rows [key0, key0 + SUB) of a head's [N, D] bf16 matrix into a
+// swizzled LDS tile.  Rows past N read as zeros (their scores are masked to
+// -inf, so they carry no weight).
+template <int BS, int D>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, int key0, char* tile, int wave,
+                                         const uint32_t (&off)[Cfg<BS, D>::LOADS]) {
+  using C = Cfg<BS, D>;
+  const uint32_t base = (uint32_t)key0 * (D * 2);
+#pragma unroll
+  for (int it = 0; it < C::LOADS; ++it) lds_dma16(rsrc, base + off[it], tile + (it * C::NW + wave) * 64 * 16);
+}
+
+// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.  The K operand
+// reads run AHEAD k-steps in front of the MFMAs; scheduling fences keep that
+// order (the default schedule reuses one register set and waits out each read).
 template <int BS, int D, int NT, class C = Cfg<BS, D>>
 __device__ __forceinline__ void scores(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&st)[NT], int t0,
                                        int l32, int hf) {
+  constexpr int AHEAD = C::DS < 3 ? C::DS : 3;
+  bf16x8 kf[C::DS][NT];
+  auto read_k = [&](int ds) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) st[t][v2] = 0.f;
-  auto read_k = [&](int ds, int t) {
-    const int row = (t0 + t) * 32 + l32;
-    const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
-    return *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+    for (int t = 0; t < NT; ++t) {
+      const int row = (t0 + t) * 32 + l32;
+      const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
+      kf[ds][t] = *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+    }
   };
-  bf16x8 cur[NT], nxt[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) cur[t] = read_k(0, t);
+  for (int ds = 0; ds < AHEAD; ++ds) read_k(ds);
+  const floatx16 zero = {};
 #pragma unroll
   for (int ds = 0; ds < C::DS; ++ds) {
-    if (ds + 1 < C::DS) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (ds + AHEAD < C::DS) read_k(ds + AHEAD);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) nxt[t] = read_k(ds + 1, t);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[t], qf[ds], st[t], 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
+    for (int t = 0; t < NT; ++t)
+      st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][t], qf[ds], ds == 0 ? zero : st[t], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Online-softmax update and O^T += V^T P^T for the KC 32-key tiles t0 ..
@@ -158,15 +176,44 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, c
                                            float& m_run, float& l_run, float& ls_blk, floatx16 (&acc)[C::DT],
                                            int lane) {
   const int hf = lane >> 5;
+  // O^T += V^T P^T, steps ordered (t, h2, dt) so that consecutive MFMAs
+  // update different accumulators.  Source-lane role in the transposing read:
+  // lane 16G + 4t + g points at key row (.. + 8x + 4(G/2) + t), dims
+  // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
+  // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.  The first AHEAD
+  // steps' V operands are read before the softmax so that its VALU work
+  // covers their latency.
+  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
+  constexpr int NSTEP = C::KC * 2 * C::DT, AHEAD = NSTEP < 3 ? NSTEP : 3;
+  bf16x8 vf[NSTEP];
+  auto read_v = [&](int step) {
+    const int dt = step % C::DT, h2 = (step / C::DT) & 1, t = step / (2 * C::DT);
+    const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
+    short4_t t4[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
+      const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
+      t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
+    }
+    // whole-register reinterpretation (element-wise casts of the transposed
+    // halves are mis-assembled by the compiler)
+    vf[step] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+#pragma unroll
+  for (int step = 0; step < AHEAD; ++step) read_v(step);
+  __builtin_amdgcn_sched_barrier(0);
+
   // mask keys past the end of the sequence (partial last block) or of an
   // invalid entry: a select against the wave-uniform valid-key count
   if (nvk < C::SUB) {
+    const int lim = nvk - 4 * hf;        // key (t0+t)*32 + 8(v2/4) + 4hf + v2%4 is valid iff below nvk
 #pragma unroll
     for (int t = 0; t < C::KC; ++t)
 #pragma unroll
       for (int v2 = 0; v2 < 16; ++v2) {
-        const int kl = (t0 + t) * 32 + 8 * (v2 >> 2) + 4 * hf + (v2 & 3);
-        st[s0 + t][v2] = kl < nvk ? st[s0 + t][v2] : -INFINITY;
+        const int kl = (t0 + t) * 32 + 8 * (v2 >> 2) + (v2 & 3);
+        st[s0 + t][v2] = kl < lim ? st[s0 + t][v2] : -INFINITY;
       }
   }
   // The running max is only raised when some lane's new max exceeds it by
@@ -209,34 +256,14 @@ __device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, c
   l_run += ls;
   ls_blk += ls;
 
-  // O^T += V^T P^T.  Source-lane role in the transposing read: lane
-  // 16G + 4t + g points at key row (.. + 8x + 4(G/2) + t), dims
-  // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
-  // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.
-  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
-  auto read_v = [&](int step) {          // step = (dt * KC + t) * 2 + h2
-    const int h2 = step & 1, t = (step >> 1) % C::KC, dt = (step >> 1) / C::KC;
-    const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
-    short4_t t4[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
-      const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
-      t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
-    }
-    // whole-register reinterpretation (element-wise casts of the transposed
-    // halves are mis-assembled by the compiler)
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  constexpr int NSTEP = C::DT * C::KC * 2;
-  bf16x8 cur = read_v(0);
 #pragma unroll
   for (int step = 0; step < NSTEP; ++step) {
-    const bf16x8 nxt = step + 1 < NSTEP ? read_v(step + 1) : cur;     // read one step ahead
-    const int h2 = step & 1, t = (step >> 1) % C::KC, dt = (step >> 1) / C::KC;
-    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pb[t][h2], acc[dt], 0, 0, 0);
-    cur = nxt;
+    __builtin_amdgcn_sched_barrier(0);
+    if (step + AHEAD < NSTEP) read_v(step + AHEAD);
+    const int dt = step % C::DT, h2 = (step / C::DT) & 1, t = step / (2 * C::DT);
+    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], pb[t][h2], acc[dt], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int BS, int D>
@@ -258,7 +285,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   // length; keeping neighbouring rows on one XCD's L2 measured no faster).
   const int r = blockIdx.x;
   const int bh = r / nb, i = r - bh * nb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int l32 = lane & 31, hf = lane >> 5;
   const int q0 = i * BS;
   const int nq = min(BS, N - q0);
@@ -271,8 +299,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   if (e_begin > e_end) e_begin = e_end;
   const int n_e = (int)(e_end - e_begin);
 
-  const __bf16* kh = k + (size_t)bh * N * D;
-  const __bf16* vh = v + (size_t)bh * N * D;
+  const auto kh = head_rsrc(k + (size_t)bh * N * D, N, D);
+  const auto vh = head_rsrc(v + (size_t)bh * N * D, N, D);
 
   // Q^T fragments (B operand): lane holds query qloc, d = ds*16 + hf*8 .. +8
   bf16x8 qf[C::DS];
@@ -303,11 +331,17 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
     return key0;
   };
+  uint32_t koff[C::LOADS], voff[C::LOADS];
+#pragma unroll
+  for (int it = 0; it < C::LOADS; ++it) {
+    koff[it] = dma_src_off<BS, D, false>(it, wave, lane);
+    voff[it] = dma_src_off<BS, D, true>(it, wave, lane);
+  }
   if (n_u > 0) {
     int nv;
     const int key0 = unit_src(0, nv);
-    dma_tile<BS, D, false>(kh, key0, N, k0s, wave, lane);
-    dma_tile<BS, D, true>(vh, key0, N, v0s, wave, lane);
+    dma_tile<BS, D>(kh, key0, k0s, wave, koff);
+    dma_tile<BS, D>(vh, key0, v0s, wave, voff);
   }
   float ls_blk = 0.f;      // current entry's sum of exp2(s - m_run), for the block mass
 
@@ -321,8 +355,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     if (u + 1 < n_u) {
       int nn;
       const int key1 = unit_src(u + 1, nn);
-      dma_tile<BS, D, false>(kh, key1, N, kn, wave, lane);
-      dma_tile<BS, D, true>(vh, key1, N, vn, wave, lane);
+      dma_tile<BS, D>(kh, key1, kn, wave, koff);
+      dma_tile<BS, D>(vh, key1, vn, wave, voff);
     }
 #pragma unroll
     for (int c0 = 0; c0 < C::KU; c0 += C::KC) {
