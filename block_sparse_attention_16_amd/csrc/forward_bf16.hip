@@ -8,8 +8,7 @@
 //
 // Workgroup = one mask row (query block i of head bh), BS/32 waves.  Wave w
 // owns queries [32w, 32w + 32) of the block and every key of each visited key
-// block, with its own online-softmax state.  Two workgroups share a CU so that
-// one's softmax (VALU) overlaps the other's matrix work.
+// block, with its own online-softmax state.  Two waves share each SIMD.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = K rows from LDS, B = Q^T held in registers.  In the 32x32 accumulator a
@@ -20,18 +19,25 @@
 // from the row-major V tile with two ds_read_b64_tr_b16, which transpose
 // 4x4 blocks of bf16 across each 16-lane group.
 //
-// K and V tiles stream from HBM/L2 straight into LDS with
-// global_load_lds_dwordx4.  D = 64: two stages (double buffer).  D = 128: one
-// K tile and one V tile (64 KB, so two workgroups fit a CU); the DMA of the
-// next K tile overlaps this block's softmax and PV, the next V tile overlaps
-// the next block's scores.  LDS rows are XOR-swizzled in 16-byte chunks so
-// the MFMA operand reads are bank-conflict free.
+// Keys are consumed in units of SUB keys (a sub-block of one CSR entry).  The
+// loop is software-pipelined by one unit inside each wave: while the matrix
+// cores compute the scores of unit u+1, the VALU turns the scores of unit u
+// into probabilities; while they accumulate unit u's P V, the VALU takes the
+// row max of unit u+1.  So the softmax runs under the MFMAs of the same wave.
+//
+// K and V tiles stream from HBM/L2 straight into LDS with buffer loads (two
+// K slots, two V slots).  At the top of iteration u one barrier frees the K
+// slot of unit u (scored in iteration u-1) and the V slot of unit u-1; the
+// DMAs of K[u+2] and V[u+1] then have a whole iteration to land.  LDS rows are
+// XOR-swizzled in 16-byte chunks so the MFMA operand reads are conflict free.
 //
 // Block mass: for every visited entry e and query q the kernel stores the
 // block-local log2-sum-exp m + log2(l_block) (exact whatever the running max
 // m is); once the row's final LSE is known the epilogue turns these into
 // mean_q exp2(c_e(q) - lse2(q)).
 #include "bsa_internal.h"
+
+#include <type_traits>
 
 namespace bsa {
 namespace {
@@ -98,16 +104,13 @@ struct Cfg {
   static constexpr int NW = BS / 32;                  // waves; wave w owns 32 queries
   static constexpr int THREADS = NW * 64;
   static constexpr int WG_PER_CU = 8 / NW;            // two waves per SIMD
-  // Key blocks stream through LDS in sub-blocks of SUB keys, double-buffered;
-  // each sub-block is scored and folded into the softmax in chunks of KC
-  // 32-key tiles (KC*16 score registers per lane).
-  static constexpr int SUB = D == 64 ? BS : (BS == 128 ? 64 : 32);
-  static constexpr int U = BS / SUB;                  // sub-blocks per key block
-  static constexpr int KU = SUB / 32;                 // 32-key tiles per sub-block
-  static constexpr int KC = KU < 2 ? KU : 2;          // tiles per softmax chunk
+  // Keys stream through LDS in units of SUB keys (KC 32-key tiles).
+  static constexpr int SUB = (BS == 64 && D == 128) ? 32 : 64;
+  static constexpr int KC = SUB / 32;
+  static constexpr int U = BS / SUB;                  // units per key block
   static constexpr int DS = D / 16, DT = D / 32;      // MFMA k-steps over d, d tiles
   static constexpr int CPR = D / 8;                   // 16-byte chunks per K or V row
-  static constexpr int TILE_BYTES = SUB * D * 2;      // one K or V sub-tile
+  static constexpr int TILE_BYTES = SUB * D * 2;      // one K or V tile
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);  // dma ops per thread per tile
   static_assert(LOADS * 16 * THREADS == TILE_BYTES, "tile must split evenly over the waves");
   static_assert(4 * TILE_BYTES * WG_PER_CU <= 160 * 1024, "LDS of the resident workgroups");
@@ -138,130 +141,141 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, int key0, 
   for (int it = 0; it < C::LOADS; ++it) lds_dma16(rsrc, base + off[it], tile + (it * C::NW + wave) * 64 * 16);
 }
 
-// S^T for 32-key tiles [t0, t0 + NT) of the K tile in LDS.  The K operand
-// reads run AHEAD k-steps in front of the MFMAs; scheduling fences keep that
-// order (the default schedule reuses one register set and waits out each read).
-template <int BS, int D, int NT, class C = Cfg<BS, D>>
-__device__ __forceinline__ void scores(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&st)[NT], int t0,
-                                       int l32, int hf) {
-  constexpr int AHEAD = C::DS < 3 ? C::DS : 3;
-  bf16x8 kf[C::DS][NT];
-  auto read_k = [&](int ds) {
+// K operand of score step s = ds * KC + t: rows 32t + l32 of the tile, d
+// columns 16 ds + 8 hf .. +8.
+template <int BS, int D, class C = Cfg<BS, D>>
+__device__ __forceinline__ bf16x8 read_k(const char* ks, int s, int l32, int hf) {
+  const int ds = s / C::KC, t = s % C::KC;
+  const int row = t * 32 + l32;
+  const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
+  return *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+}
+
+// V^T operand of PV step s, steps ordered (t, h2, dt) so that consecutive
+// MFMAs update different accumulators.  Source-lane role in the transposing
+// read: lane 16G + 4r + g points at key row (32t + 16h2 + 8x + 4(G/2) + r),
+// dims 32dt + 16(G&1) + 4g .. +3, so that result lane L receives
+// V[32t + 16h2 + 8x + 4(L/32) + r][32dt + L%32] for r = 0..3.
+template <int BS, int D, class C = Cfg<BS, D>>
+__device__ __forceinline__ bf16x8 read_v(const char* vs, int s, int lane) {
+  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
+  const int dt = s % C::DT, h2 = (s / C::DT) & 1, t = s / (2 * C::DT);
+  const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
+  short4_t t4[2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int row = (t0 + t) * 32 + l32;
-      const int c = (ds * 2 + hf) ^ swz_k<C::CPR>(row);
-      kf[ds][t] = *reinterpret_cast<const bf16x8*>(ks + (row * C::CPR + c) * 16);
+  for (int x = 0; x < 2; ++x) {
+    const int row = t * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
+    const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
+    t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
+  }
+  // whole-register reinterpretation (element-wise casts of the transposed
+  // halves are mis-assembled by the compiler)
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Keys past the valid count of a unit (end of the sequence, or an invalid
+// entry) get score -inf.  nvk is wave-uniform.
+template <int BS, int D, class C = Cfg<BS, D>>
+__device__ __forceinline__ void mask_scores(floatx16 (&s)[C::KC], int nvk, int hf) {
+  const int lim = nvk - 4 * hf;        // key 32t + 8(v/4) + 4hf + v%4 is valid iff below nvk
+#pragma unroll
+  for (int t = 0; t < C::KC; ++t)
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) {
+      const int kl = t * 32 + 8 * (v2 >> 2) + (v2 & 3);
+      s[t][v2] = kl < lim ? s[t][v2] : -INFINITY;
     }
-  };
-#pragma unroll
-  for (int ds = 0; ds < AHEAD; ++ds) read_k(ds);
+}
+
+// Scores of one unit alone (pipeline prologue).
+template <int BS, int D, class C = Cfg<BS, D>>
+__device__ __forceinline__ void scores_only(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&sn)[C::KC],
+                                            int l32, int hf) {
+  constexpr int NS = C::DS * C::KC;
   const floatx16 zero = {};
+  bf16x8 kf[NS];
 #pragma unroll
-  for (int ds = 0; ds < C::DS; ++ds) {
+  for (int s = 0; s < NS; ++s) kf[s] = read_k<BS, D>(ks, s, l32, hf);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int ds = s / C::KC, t = s % C::KC;
+    sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[ds], ds == 0 ? zero : sn[t], 0, 0, 0);
+  }
+}
+
+// Probabilities j in [j0, j1) of the current unit: exp2 of the scaled,
+// max-shifted scores (in place), their running sum, and bf16 copies (pairs)
+// for the PV MFMAs.
+template <int BS, int D, class C = Cfg<BS, D>>
+__device__ __forceinline__ void probs(floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float c2, float m_use,
+                                      float& ls, int j0, int j1) {
+#pragma unroll
+  for (int j = j0; j < j1; ++j) {
+    const int t = j / 16, v2 = j % 16;
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][v2], c2, -m_use));
+    sc[t][v2] = p;
+    ls += p;
+    if (j & 1) {
+      pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)sc[t][v2 - 1];
+      pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+    }
+  }
+}
+
+// Phase B of an iteration: probabilities of the current unit, interleaved
+// with the score MFMAs of the next unit when NEXT.  Scheduling
+// fences pin the interleave: per MFMA step one K read (AHEAD steps ahead)
+// and an equal share of the exponentials.
+template <int BS, int D, bool NEXT, class C = Cfg<BS, D>>
+__device__ __forceinline__ void phase_b(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&sc)[C::KC],
+                                        floatx16 (&sn)[C::KC], bf16x8 (&pb)[C::KC][2], float c2, float m_use,
+                                        float& ls, int l32, int hf) {
+  constexpr int NS = C::DS * C::KC;            // score MFMAs of the next unit
+  constexpr int NE = C::KC * 16;               // probabilities per lane
+  constexpr int NSEG = NEXT ? NS : 1;
+  constexpr int EPS = (NE + NSEG - 1) / NSEG;
+  constexpr int AHEAD = NS < 2 ? NS : 2;
+  const floatx16 zero = {};
+  bf16x8 kf[NS];
+  if constexpr (NEXT) {
+#pragma unroll
+    for (int s = 0; s < AHEAD; ++s) kf[s] = read_k<BS, D>(ks, s, l32, hf);
+  }
+#pragma unroll
+  for (int g = 0; g < NSEG; ++g) {
     __builtin_amdgcn_sched_barrier(0);
-    if (ds + AHEAD < C::DS) read_k(ds + AHEAD);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][t], qf[ds], ds == 0 ? zero : st[t], 0, 0, 0);
+    if constexpr (NEXT) {
+      if (g + AHEAD < NS) kf[g + AHEAD] = read_k<BS, D>(ks, g + AHEAD, l32, hf);
+      const int ds = g / C::KC, t = g % C::KC;
+      sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ds], ds == 0 ? zero : sn[t], 0, 0, 0);
+    }
+    probs<BS, D>(sc, pb, c2, m_use, ls, g * EPS, (g + 1) * EPS < NE ? (g + 1) * EPS : NE);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Online-softmax update and O^T += V^T P^T for the KC 32-key tiles t0 ..
-// t0 + KC - 1 of the sub-tile, whose scores are st[s0 ..].  nvk = valid keys
-// in the sub-tile (wave-uniform).
-template <int BS, int D, int NT, class C = Cfg<BS, D>>
-__device__ __forceinline__ void softmax_pv(floatx16 (&st)[NT], int s0, int t0, const char* vs, int nvk, float c2,
-                                           float& m_run, float& l_run, float& ls_blk, floatx16 (&acc)[C::DT],
-                                           int lane) {
-  const int hf = lane >> 5;
-  // O^T += V^T P^T, steps ordered (t, h2, dt) so that consecutive MFMAs
-  // update different accumulators.  Source-lane role in the transposing read:
-  // lane 16G + 4t + g points at key row (.. + 8x + 4(G/2) + t), dims
-  // dt*32 + 16(G&1) + 4g .. +3, so that result lane L receives
-  // V[.. + 8x + 4(L/32) + t][dt*32 + L%32] for t = 0..3.  The first AHEAD
-  // steps' V operands are read before the softmax so that its VALU work
-  // covers their latency.
-  const int G = lane >> 4, tr = (lane >> 2) & 3, g4 = lane & 3;
-  constexpr int NSTEP = C::KC * 2 * C::DT, AHEAD = NSTEP < 3 ? NSTEP : 3;
+// Phase C: O^T += V^T P^T for the current unit, interleaved with the row max
+// of the next unit's scores when NEXT.  V operands are read AHEAD steps ahead.
+template <int BS, int D, bool NEXT, class C = Cfg<BS, D>>
+__device__ __forceinline__ void phase_c(const char* vs, const bf16x8 (&pb)[C::KC][2], floatx16 (&acc)[C::DT],
+                                        const floatx16 (&sn)[C::KC], float& mx, int lane) {
+  constexpr int NSTEP = C::KC * 2 * C::DT;
+  constexpr int NM = C::KC * 16;
+  constexpr int MPS = (NM + NSTEP - 1) / NSTEP;   // max operands per step
+  constexpr int AHEAD = NSTEP < 3 ? NSTEP : 3;
   bf16x8 vf[NSTEP];
-  auto read_v = [&](int step) {
-    const int dt = step % C::DT, h2 = (step / C::DT) & 1, t = step / (2 * C::DT);
-    const int dcol = dt * 32 + 16 * (G & 1) + 4 * g4;
-    short4_t t4[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int row = (t0 + t) * 32 + h2 * 16 + 8 * x + 4 * (G >> 1) + tr;
-      const int c = (dcol >> 3) ^ swz_v<C::CPR>(row);
-      t4[x] = lds_read_tr16(vs + (row * C::CPR + c) * 16 + (dcol & 7) * 2);
-    }
-    // whole-register reinterpretation (element-wise casts of the transposed
-    // halves are mis-assembled by the compiler)
-    vf[step] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  for (int s = 0; s < AHEAD; ++s) vf[s] = read_v<BS, D>(vs, s, lane);
 #pragma unroll
-  for (int step = 0; step < AHEAD; ++step) read_v(step);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // mask keys past the end of the sequence (partial last block) or of an
-  // invalid entry: a select against the wave-uniform valid-key count
-  if (nvk < C::SUB) {
-    const int lim = nvk - 4 * hf;        // key (t0+t)*32 + 8(v2/4) + 4hf + v2%4 is valid iff below nvk
-#pragma unroll
-    for (int t = 0; t < C::KC; ++t)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) {
-        const int kl = (t0 + t) * 32 + 8 * (v2 >> 2) + (v2 & 3);
-        st[s0 + t][v2] = kl < lim ? st[s0 + t][v2] : -INFINITY;
-      }
-  }
-  // The running max is only raised when some lane's new max exceeds it by
-  // more than kTau (log2 units): p <= 2^kTau stays safe in bf16/fp32 and most
-  // updates skip the rescale of the output accumulators.  Exact for any m_run.
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < C::KC; ++t)
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, st[s0 + t][v2]);
-  mx = xhalf_max(mx) * c2;
-  if (__any(mx > m_run + kTau)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
-    l_run *= alpha;
-    ls_blk *= alpha;
-  }
-  const float m_use = m_run == -INFINITY ? 0.f : m_run;
-  bf16x8 pb[C::KC][2];
-  float ls = 0.f;
-#pragma unroll
-  for (int t = 0; t < C::KC; ++t) {
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(st[s0 + t][v2], c2, -m_use));
-      st[s0 + t][v2] = p;
-      ls += p;
-    }
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) pb[t][h2][e2] = (__bf16)st[s0 + t][h2 * 8 + e2];
-  }
-  ls = xhalf_sum(ls);
-  l_run += ls;
-  ls_blk += ls;
-
-#pragma unroll
-  for (int step = 0; step < NSTEP; ++step) {
+  for (int s = 0; s < NSTEP; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-    if (step + AHEAD < NSTEP) read_v(step + AHEAD);
-    const int dt = step % C::DT, h2 = (step / C::DT) & 1, t = step / (2 * C::DT);
-    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], pb[t][h2], acc[dt], 0, 0, 0);
+    if (s + AHEAD < NSTEP) vf[s + AHEAD] = read_v<BS, D>(vs, s + AHEAD, lane);
+    const int dt = s % C::DT, h2 = (s / C::DT) & 1, t = s / (2 * C::DT);
+    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], pb[t][h2], acc[dt], 0, 0, 0);
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int j = s * MPS; j < (s + 1) * MPS && j < NM; ++j) mx = fmaxf(mx, sn[j / 16][j % 16]);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -275,8 +289,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
   // the compiler see that reads of one tile do not wait on the DMA into another.
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
   __shared__ float lse2_s[BS];
 
@@ -320,61 +334,118 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  float ls_blk = 0.f;      // current entry's sum of exp2(s - m_run), for the block mass
   const float c2 = scale * kLog2e;   // logits in base-2 units
 
-  // Unit u = sub-block (u % U) of CSR entry (u / U).
+  // Unit u = sub-block (u % U) of CSR entry (u / U).  The loop reads the
+  // entries' key-block ids with vector buffer loads one iteration ahead (so
+  // they land under the same wait as the tile DMAs, and ids past the row read
+  // as 0 without a bounds test); the prologue reads its first ids directly.
   const int n_u = n_e * C::U;
-  auto unit_src = [&](int u, int& nvk) {      // first key of the unit; nvk = its valid keys
-    const int j_raw = col_idx[e_begin + u / C::U];
+  const auto colr = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col_idx + e_begin), (short)0, n_e * 4,
+                                                      0x00020000);
+  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / C::U) * 4, 0, 0); };
+  auto unit_key = [&](int j_raw, int u, int& nvk) {   // first key of unit u; nvk = its valid keys
     const bool valid = j_raw >= 0 && j_raw < nb;
     const int key0 = (valid ? j_raw : 0) * BS + (u % C::U) * C::SUB;
     nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
     return key0;
   };
+  auto unit_src = [&](int u, int& nvk) { return unit_key(col_idx[e_begin + u / C::U], u, nvk); };
   uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
   for (int it = 0; it < C::LOADS; ++it) {
     koff[it] = dma_src_off<BS, D, false>(it, wave, lane);
     voff[it] = dma_src_off<BS, D, true>(it, wave, lane);
   }
+
+  // Fold a unit's row max (raw score units, this lane's half) into the
+  // running max.  It is only raised when some lane's new max exceeds it by
+  // more than kTau (log2 units): p <= 2^kTau stays safe in bf16/fp32 and most
+  // updates skip the rescale of the output accumulators.  Exact for any m_run.
+  auto fold_max = [&](float mx) __attribute__((always_inline)) {
+    mx = xhalf_max(mx) * c2;
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
+      l_run *= alpha;
+      ls_blk *= alpha;
+    }
+  };
+
+  floatx16 sa[C::KC], sb[C::KC];     // scores of the current and the next unit
+  int jv1 = col_load(1), jv2 = col_load(2);   // key-block ids of units u+1, u+2 (VGPR, uniform)
   if (n_u > 0) {
-    int nv;
-    const int key0 = unit_src(0, nv);
+    int nv0;
+    const int key0 = unit_src(0, nv0);
     dma_tile<BS, D>(kh, key0, k0s, wave, koff);
     dma_tile<BS, D>(vh, key0, v0s, wave, voff);
-  }
-  float ls_blk = 0.f;      // current entry's sum of exp2(s - m_run), for the block mass
-
-  // One unit: wait for its tiles, start the DMA of the next unit into the
-  // other stage, then score and fold it into the softmax chunk by chunk.
-  auto do_unit = [&](const char* ks, const char* vs, char* kn, char* vn, int u) __attribute__((always_inline)) {
-    int nvk;
-    unit_src(u, nvk);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA into the current stage landed
-    __syncthreads();                      // ... and every other wave's
-    if (u + 1 < n_u) {
-      int nn;
-      const int key1 = unit_src(u + 1, nn);
-      dma_tile<BS, D>(kh, key1, kn, wave, koff);
-      dma_tile<BS, D>(vh, key1, vn, wave, voff);
+    if (n_u > 1) {
+      int nv1;
+      dma_tile<BS, D>(kh, unit_src(1, nv1), k1s, wave, koff);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    scores_only<BS, D>(k0s, qf, sa, l32, hf);
+    if (nv0 < C::SUB) mask_scores<BS, D>(sa, nv0, hf);
+    float mx = -INFINITY;
 #pragma unroll
-    for (int c0 = 0; c0 < C::KU; c0 += C::KC) {
-      floatx16 sh[C::KC];
-      scores<BS, D, C::KC>(ks, qf, sh, c0, l32, hf);
-      softmax_pv<BS, D, C::KC>(sh, 0, c0, vs, nvk, c2, m_run, l_run, ls_blk, acc, lane);
-    }
-    if (u % C::U == C::U - 1) {         // last sub-block of the entry
+    for (int t = 0; t < C::KC; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, sa[t][v2]);
+    fold_max(mx);
+  }
+
+  // Iteration u: K[u+1] sits in slot (u+1)%2, V[u] in slot u%2.  sc holds
+  // unit u's scores (masked, max folded in); sn receives unit u+1's.  Inside
+  // the unrolled loop the next unit's scores are always computed (for the
+  // last unit from a stale K slot, then discarded), which keeps one code path.
+  auto iter = [&](auto next_tag, int u, floatx16 (&sc)[C::KC], floatx16 (&sn)[C::KC], const char* ks_next,
+                  const char* vs_cur, char* k_free, char* v_free) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMAs of K[u+1], V[u] (and ids) landed
+    __syncthreads();                      // ... and every other wave's; slots of K[u], V[u-1] are free
+    const bool has_next = u + 1 < n_u;
+    int nvn, nn;
+    const int key1 = unit_key(__builtin_amdgcn_readfirstlane(jv1), u + 1, nvn);
+    const int key2 = unit_key(__builtin_amdgcn_readfirstlane(jv2), u + 2, nn);
+    if (u + 2 < n_u) dma_tile<BS, D>(kh, key2, k_free, wave, koff);
+    if (has_next) dma_tile<BS, D>(vh, key1, v_free, wave, voff);
+    jv1 = jv2;
+    jv2 = col_load(u + 3);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pb[C::KC][2];
+    float ls = 0.f;
+    phase_b<BS, D, NEXT>(ks_next, qf, sc, sn, pb, c2, m_use, ls, l32, hf);
+    ls = xhalf_sum(ls);
+    l_run += ls;
+    ls_blk += ls;
+    if (u % C::U == C::U - 1) {         // last unit of the entry
       const int it = u / C::U;
       if (part != nullptr && hf == 0)
         part[(e_begin + it) * BS + qloc] = ls_blk > 0.f ? m_run + __builtin_amdgcn_logf(ls_blk) : -INFINITY;
       ls_blk = 0.f;
     }
+    float mx = -INFINITY;
+    if constexpr (NEXT) {
+      if (has_next && nvn < C::SUB) mask_scores<BS, D>(sn, nvn, hf);
+    }
+    phase_c<BS, D, NEXT>(vs_cur, pb, acc, sn, mx, lane);
+    if constexpr (NEXT) fold_max(has_next ? mx : -INFINITY);   // a stale next unit adds nothing
   };
-  for (int u = 0; u < n_u; u += 2) {
-    do_unit(k0s, v0s, k1s, v1s, u);
-    if (u + 1 < n_u) do_unit(k1s, v1s, k0s, v0s, u + 1);
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  int u = 0;
+  for (; u + 1 < n_u; u += 2) {
+    iter(Yes{}, u, sa, sb, k1s, v0s, k0s, v1s);
+    iter(Yes{}, u + 1, sb, sa, k0s, v1s, k1s, v0s);
   }
+  if (u < n_u) iter(No{}, u, sa, sb, k1s, v0s, k0s, v1s);
 
   // ---- normalise, write O and LSE ----
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
