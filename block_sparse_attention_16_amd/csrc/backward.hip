@@ -23,6 +23,13 @@
 // (two ds_read_b64_tr_b16), the 32x32 accumulator of a lane holding one
 // column and 16 rows {8a + 4h + r}, and the k-slot permutation that lets an
 // accumulator, rounded to bf16, feed the next MFMA as its B operand.
+//
+// Like the forward, both MFMA kernels walk their blocks in units of SUB rows
+// of the streamed operand, double-buffered in LDS and filled with buffer
+// loads straight into LDS (exact LDS wait counts while a copy is in flight;
+// reads past the end return zeros); block ids come one unit ahead through
+// vector loads; operand reads run ahead of the MFMAs under scheduling fences.
+// Units are small enough for two waves per SIMD.
 #include <type_traits>
 
 #include "bsa_internal.h"
@@ -50,36 +57,59 @@ __device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
 }
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at base; reads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 (or 4) bytes per lane from buffer offset `off` into LDS at
+// lds_wave_base + 16 (or 4) * lane.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0,
+                                           0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, off, 0,
+                                           0, 0);
 }
 
 template <int BS, int D>
 struct BCfg {
   static constexpr int NW = BS / 32;          // waves; wave w owns 32 rows (queries or keys)
   static constexpr int THREADS = NW * 64;
-  static constexpr int T32 = BS / 32;         // 32-wide tiles per block
+  static constexpr int SUB = (BS == 64 && D == 128) ? 32 : 64;   // streamed rows per unit
+  static constexpr int KC = SUB / 32;         // 32-row tiles per unit
+  static constexpr int U = BS / SUB;          // units per block
   static constexpr int DS = D / 16, DT = D / 32;
   static constexpr int CPR = D / 8;
-  static constexpr int TILE_BYTES = BS * D * 2;
+  static constexpr int TILE_BYTES = SUB * D * 2;
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);
   static_assert(LOADS * 16 * THREADS == TILE_BYTES, "tile must split evenly over the waves");
+  static_assert(4 * TILE_BYTES * (8 / NW) <= 160 * 1024, "LDS of two waves per SIMD");
 };
 
-// DMA rows [row0, row0 + BS) of two [N, D] bf16 matrices into swizzled LDS
-// tiles (rows past N repeat row N-1).
+// Per-lane byte offset, within a SUB-row window of a [N, D] bf16 matrix, of
+// the 16-byte chunk that dma op `it` of this lane stores (lane l of a wave
+// writes LDS chunk base + l; the swizzle decides which logical chunk lands there).
 template <int BS, int D>
-__device__ __forceinline__ void dma_tiles(const __bf16* __restrict__ a, const __bf16* __restrict__ b, int row0,
-                                          int N, char* ta, char* tb, int wave, int lane) {
+__device__ __forceinline__ uint32_t dma_src_off(int it, int wave, int lane) {
   using C = BCfg<BS, D>;
+  const int L = (it * C::NW + wave) * 64 + lane;
+  const int row = L / C::CPR, pos = L % C::CPR;
+  return (uint32_t)((row * D + (pos ^ swz<C::CPR>(row)) * 8) * 2);
+}
+
+// DMA rows [row0, row0 + SUB) of two heads' [N, D] bf16 matrices into
+// swizzled LDS tiles (rows past N read as zeros).
+template <int BS, int D>
+__device__ __forceinline__ void dma_tiles(__amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b, int row0, char* ta,
+                                          char* tb, int wave, const uint32_t (&off)[BCfg<BS, D>::LOADS]) {
+  using C = BCfg<BS, D>;
+  const uint32_t base = (uint32_t)row0 * (D * 2);
 #pragma unroll
   for (int it = 0; it < C::LOADS; ++it) {
-    const int chunk0 = (it * C::NW + wave) * 64;
-    const int L = chunk0 + lane;
-    const int row = L / C::CPR, pos = L % C::CPR;
-    const size_t src = (size_t)min(row0 + row, N - 1) * D + (pos ^ swz<C::CPR>(row)) * 8;
-    lds_dma16(a + src, ta + chunk0 * 16);
-    lds_dma16(b + src, tb + chunk0 * 16);
+    lds_dma16(a, base + off[it], ta + (it * C::NW + wave) * 64 * 16);
+    lds_dma16(b, base + off[it], tb + (it * C::NW + wave) * 64 * 16);
   }
 }
 
@@ -109,6 +139,34 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const floatx16& a, int half) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)a[half * 8 + e];
   return r;
+}
+
+// Two 32x32 accumulators of one 32-row tile: X = A1 B1 and Y = A2 B2 over
+// the d dimension, A operands read row-wise from tiles ta / tb (rows
+// r0 + l32), B operands in registers.  Reads run AHEAD k-steps in front.
+template <int D>
+__device__ __forceinline__ void two_products(const char* ta, const char* tb, const bf16x8 (&ba)[D / 16],
+                                             const bf16x8 (&bb)[D / 16], floatx16& x, floatx16& y, int r0, int l32,
+                                             int hf) {
+  constexpr int DS = D / 16, CPR = D / 8, AHEAD = 2;
+  const floatx16 zero = {};
+  bf16x8 fa[DS], fb[DS];
+#pragma unroll
+  for (int ds = 0; ds < AHEAD; ++ds) {
+    fa[ds] = read_row8<CPR>(ta, r0 + l32, ds * 2 + hf);
+    fb[ds] = read_row8<CPR>(tb, r0 + l32, ds * 2 + hf);
+  }
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (ds + AHEAD < DS) {
+      fa[ds + AHEAD] = read_row8<CPR>(ta, r0 + l32, (ds + AHEAD) * 2 + hf);
+      fb[ds + AHEAD] = read_row8<CPR>(tb, r0 + l32, (ds + AHEAD) * 2 + hf);
+    }
+    x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ds], ba[ds], ds == 0 ? zero : x, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ds], bb[ds], ds == 0 ? zero : y, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,7 +259,7 @@ __global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ ro
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query block (mask row).  Wave w owns queries
-// [32w, 32w+32); per visited key block j (tiles K_j, V_j in LDS):
+// [32w, 32w+32); per unit (SUB keys of a visited key block, tiles K, V in LDS):
 //   S^T = K Q^T, P^T = exp2(c2 S^T - lse2_q), dP^T = V dO^T.
 // Pass 1 accumulates delta_q = sum_k P dP over the row in fp32 (equal to
 // dO_q . O_q for the exact O, without the rounding of a bf16 O) and stores it
@@ -209,7 +267,7 @@ __global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ ro
 // dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int BS, int D>
-__global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
+__global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
@@ -222,7 +280,8 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
 
   const int r = blockIdx.x;
   const int bh = r / nb, i = r - bh * nb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int qloc = wave * 32 + l32;
   const int qq = i * BS + qloc;
@@ -231,8 +290,10 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
   if (e_begin < 0) e_begin = 0;
   if (e_begin > e_end) e_begin = e_end;
   const int n_e = (int)(e_end - e_begin);
-  const __bf16* kh = k + (size_t)bh * N * D;
-  const __bf16* vh = v + (size_t)bh * N * D;
+  const int n_u = n_e * C::U;
+  const auto kh = raw_rsrc(k + (size_t)bh * N * D, N * D * 2);
+  const auto vh = raw_rsrc(v + (size_t)bh * N * D, N * D * 2);
+  const auto colr = raw_rsrc(col_idx + e_begin, n_e * 4);
 
   bf16x8 qf[C::DS], gf[C::DS];     // Q^T and dO^T as B operands (query column qloc)
   {
@@ -248,82 +309,92 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
   const float c2 = scale * kLog2e;
   float my_delta = 0.f;
 
+  uint32_t off[C::LOADS];
+#pragma unroll
+  for (int it = 0; it < C::LOADS; ++it) off[it] = dma_src_off<BS, D>(it, wave, lane);
+
   floatx16 acc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
-  auto prologue = [&]() {
-    if (n_e > 0) {
-      const int j0 = col_idx[e_begin];
-      dma_tiles<BS, D>(kh, vh, ((j0 >= 0 && j0 < nb) ? j0 : 0) * BS, N, k0s, v0s, wave, lane);
-    }
+  // first key and valid-key count of unit u from its block id
+  auto unit_key = [&](int j_raw, int u, int& nvk) {
+    const bool valid = j_raw >= 0 && j_raw < nb;
+    const int key0 = (valid ? j_raw : 0) * BS + (u % C::U) * C::SUB;
+    nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
+    return key0;
   };
+  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / C::U) * 4, 0, 0); };
 
   // SECOND = false: accumulate sum_k P dP into dsum; true: dS and dQ.
-  auto do_block = [&](auto second, const char* ks, const char* vs, char* kn, char* vn, int it, float& dsum)
-                      __attribute__((always_inline)) {
-    const int64_t e = e_begin + it;
-    const int j_raw = col_idx[e];
-    const bool valid = j_raw >= 0 && j_raw < nb;
-    const int j = valid ? j_raw : 0;
-    const int nvk = valid ? min(BS, N - j * BS) : 0;   // valid keys in this block
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    if (it + 1 < n_e) {
-      const int jn = col_idx[e + 1];
-      dma_tiles<BS, D>(kh, vh, ((jn >= 0 && jn < nb) ? jn : 0) * BS, N, kn, vn, wave, lane);
+  auto pass = [&](auto second, float& dsum) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    int jv0 = 0, jv1 = 0;
+    if (n_u > 0) {
+      jv0 = col_idx[e_begin];
+      int nv;
+      dma_tiles<BS, D>(kh, vh, unit_key(jv0, 0, nv), k0s, v0s, wave, off);
+      jv1 = col_load(1);
     }
-    // one 32-key tile at a time keeps only two accumulators live
+    auto unit = [&](int u, const char* ks, const char* vs, char* kn, char* vn) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies (and the next id) landed
+      __syncthreads();                      // ... and every wave's; the other slot is free
+      int nvk, nn;
+      unit_key(__builtin_amdgcn_readfirstlane(jv0), u, nvk);
+      const int key1 = unit_key(__builtin_amdgcn_readfirstlane(jv1), u + 1, nn);
+      if (u + 1 < n_u) dma_tiles<BS, D>(kh, vh, key1, kn, vn, wave, off);
+      jv0 = jv1;
+      jv1 = col_load(u + 2);
+      const int lim = nvk - 4 * hf;         // key 32t + 8(x/4) + 4hf + x%4 is valid iff below nvk
 #pragma unroll
-    for (int kt = 0; kt < C::T32; ++kt) {
-      floatx16 st, dpt;
+      for (int t = 0; t < C::KC; ++t) {
+        floatx16 st, dpt;
+        two_products<D>(ks, vs, qf, gf, st, dpt, t * 32, l32, hf);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) { st[x] = 0.f; dpt[x] = 0.f; }
+        for (int x = 0; x < 16; ++x) {
+          const int kl = t * 32 + 8 * (x >> 2) + (x & 3);
+          const float p = kl < lim ? __builtin_amdgcn_exp2f(fmaf(st[x], c2, -my_lse2)) : 0.f;
+          if constexpr (SECOND) st[x] = p * (dpt[x] - my_delta);
+          else dsum = fmaf(p, dpt[x], dsum);
+        }
+        if constexpr (SECOND) {
+          const bf16x8 ds0 = to_bf16x8(st, 0), ds1 = to_bf16x8(st, 1);
+          // step s: d tile s % DT, 16-key half s / DT (consecutive MFMAs, different accumulators)
+          constexpr int NS = 2 * C::DT, AHEAD = 2;
+          auto rd = [&](int st) { return read_tr8<C::CPR>(ks, t * 32 + 16 * (st / C::DT), (st % C::DT) * 32, lane); };
+          bf16x8 a[NS];
 #pragma unroll
-      for (int ds = 0; ds < C::DS; ++ds) {
-        const bf16x8 ka = read_row8<C::CPR>(ks, kt * 32 + l32, ds * 2 + hf);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ds], st, 0, 0, 0);
-        const bf16x8 va = read_row8<C::CPR>(vs, kt * 32 + l32, ds * 2 + hf);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ds], dpt, 0, 0, 0);
-      }
+          for (int s = 0; s < AHEAD; ++s) a[s] = rd(s);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int kl = kt * 32 + 8 * (x >> 2) + 4 * hf + (x & 3);
-        const float p = kl < nvk ? __builtin_amdgcn_exp2f(fmaf(st[x], c2, -my_lse2)) : 0.f;
-        if constexpr (decltype(second)::value) st[x] = p * (dpt[x] - my_delta);
-        else dsum = fmaf(p, dpt[x], dsum);
-      }
-      if constexpr (decltype(second)::value) {
-        const bf16x8 ds0 = to_bf16x8(st, 0), ds1 = to_bf16x8(st, 1);
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 a0 = read_tr8<C::CPR>(ks, kt * 32, dt * 32, lane);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, ds0, acc[dt], 0, 0, 0);
-          const bf16x8 a1 = read_tr8<C::CPR>(ks, kt * 32 + 16, dt * 32, lane);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, ds1, acc[dt], 0, 0, 0);
+          for (int s = 0; s < NS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + AHEAD < NS) a[s + AHEAD] = rd(s + AHEAD);
+            const int dt = s % C::DT;
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], (s / C::DT) ? ds1 : ds0, acc[dt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    int u = 0;
+    for (; u + 1 < n_u; u += 2) {
+      unit(u, k0s, v0s, k1s, v1s);
+      unit(u + 1, k1s, v1s, k0s, v0s);
     }
+    if (u < n_u) unit(u, k0s, v0s, k1s, v1s);
   };
 
   using first_t = std::integral_constant<bool, false>;
   using second_t = std::integral_constant<bool, true>;
   float dsum = 0.f;
-  prologue();
-  for (int it = 0; it < n_e; it += 2) {
-    do_block(first_t{}, k0s, v0s, k1s, v1s, it, dsum);
-    if (it + 1 < n_e) do_block(first_t{}, k1s, v1s, k0s, v0s, it + 1, dsum);
-  }
+  pass(first_t{}, dsum);
   my_delta = dsum + __shfl_xor(dsum, 32);
   if (hf == 0) delta[prow] = my_delta;
-  __syncthreads();                      // every wave is done with the stage tiles
-  prologue();
-  for (int it = 0; it < n_e; it += 2) {
-    do_block(second_t{}, k0s, v0s, k1s, v1s, it, dsum);
-    if (it + 1 < n_e) do_block(second_t{}, k1s, v1s, k0s, v0s, it + 1, dsum);
-  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // the last unit's prefetched id
+  __syncthreads();                      // every wave is done with the tiles
+  pass(second_t{}, dsum);
 
   if (qq < N) {
     __bf16* row = dq + ((size_t)bh * N + qq) * D;
@@ -341,12 +412,13 @@ __global__ __launch_bounds__(2 * BS, 1) void dq_kernel(
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per key block (bh, j).  Wave w owns keys
-// [32w, 32w+32); per query block i of column j (tiles Q_i, dO_i in LDS):
+// [32w, 32w+32); per unit (SUB queries of a query block of column j: tiles
+// Q, dO and their lse2 / delta rows in LDS):
 //   S = Q K^T, P = exp2(c2 S - lse2_q), dP = dO V^T, dS = P (dP - delta_q),
 //   dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
 template <int BS, int D>
-__global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
+__global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D = 128 needs the whole register file
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ csc_start, const int32_t* __restrict__ csc_count,
@@ -357,19 +429,24 @@ __global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
   __shared__ __attribute__((aligned(1024))) char q1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char g0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char g1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float ld0s[2 * C::SUB];   // lse2 rows, then delta rows
+  __shared__ __attribute__((aligned(16))) float ld1s[2 * C::SUB];
 
   const int c = blockIdx.x;                      // column = bh * nb + j
   const int bh = c / nb, j = c - bh * nb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int kloc = wave * 32 + l32;
   const int kk = j * BS + kloc;
   const int start = csc_start[c];
   const int n_e = csc_count[c];
-  const __bf16* qh = q + (size_t)bh * N * D;
-  const __bf16* gh = dout + (size_t)bh * N * D;
-  const float* lse2h = lse2 + (size_t)bh * nb * BS;
-  const float* delh = delta + (size_t)bh * nb * BS;
+  const int n_u = n_e * C::U;
+  const auto qh = raw_rsrc(q + (size_t)bh * N * D, N * D * 2);
+  const auto gh = raw_rsrc(dout + (size_t)bh * N * D, N * D * 2);
+  const auto lr = raw_rsrc(lse2 + (size_t)bh * nb * BS, nb * BS * 4);
+  const auto dr = raw_rsrc(delta + (size_t)bh * nb * BS, nb * BS * 4);
+  const auto rowr = raw_rsrc(csc_row + start, n_e * 4);
 
   bf16x8 kf[C::DS], vf[C::DS];     // K^T and V^T as B operands (key column kloc)
   {
@@ -383,50 +460,63 @@ __global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
   const bool kvalid = kk < N;
   const float c2 = scale * kLog2e;
 
+  uint32_t off[C::LOADS];
+#pragma unroll
+  for (int it = 0; it < C::LOADS; ++it) off[it] = dma_src_off<BS, D>(it, wave, lane);
+
   floatx16 adk[C::DT], adv[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) { adk[dt][e] = 0.f; adv[dt][e] = 0.f; }
 
-  auto qblock = [&](int it) -> int {
-    const int ib = csc_row[start + it];
-    return (ib >= 0 && ib < nb) ? ib : -1;
+  // first padded query row of unit u (-1: invalid entry)
+  auto unit_row = [&](int ib, int u) { return (ib >= 0 && ib < nb) ? ib * BS + (u % C::U) * C::SUB : -1; };
+  auto row_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(rowr, (u / C::U) * 4, 0, 0); };
+  // tiles of unit rows [row0, row0 + SUB): Q, dO, and (wave 0) the lse2 and delta rows
+  auto dma_unit = [&](int row0, char* qs, char* gs, float* ls) __attribute__((always_inline)) {
+    const int r0 = row0 < 0 ? 0 : row0;
+    dma_tiles<BS, D>(qh, gh, r0, qs, gs, wave, off);
+    if (wave == 0) {
+      if constexpr (C::SUB == 32) {
+        // lanes 0-31: lse2 rows, lanes 32-63: delta rows
+        const uint32_t o = (uint32_t)(r0 + l32) * 4;
+        if (hf == 0) lds_dma4(lr, o, ls);
+        else lds_dma4(dr, o, ls);
+      } else {
+        lds_dma4(lr, (uint32_t)(r0 + lane) * 4, ls);
+        lds_dma4(dr, (uint32_t)(r0 + lane) * 4, ls + C::SUB);
+      }
+    }
   };
-  if (n_e > 0) {
-    const int i0 = qblock(0);
-    dma_tiles<BS, D>(qh, gh, (i0 < 0 ? 0 : i0) * BS, N, q0s, g0s, wave, lane);
+
+  int iv0 = 0, iv1 = 0;
+  if (n_u > 0) {
+    iv0 = csc_row[start];
+    dma_unit(unit_row(iv0, 0), q0s, g0s, ld0s);
+    iv1 = row_load(1);
   }
 
-  auto do_block = [&](const char* qs, const char* gs, char* qn, char* gn, int it) __attribute__((always_inline)) {
-    const int ib = qblock(it);
-    const bool valid = ib >= 0 && kvalid;
-    const int i = ib < 0 ? 0 : ib;
+  auto unit = [&](int u, const char* qs, const char* gs, const float* ls, char* qn, char* gn, float* ln)
+                  __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (it + 1 < n_e) {
-      const int in = qblock(it + 1);
-      dma_tiles<BS, D>(qh, gh, (in < 0 ? 0 : in) * BS, N, qn, gn, wave, lane);
-    }
+    const bool valid = unit_row(__builtin_amdgcn_readfirstlane(iv0), u) >= 0 && kvalid;
+    const int row1 = unit_row(__builtin_amdgcn_readfirstlane(iv1), u + 1);
+    if (u + 1 < n_u) dma_unit(row1, qn, gn, ln);
+    iv0 = iv1;
+    iv1 = row_load(u + 2);
     // S and dP, one 32-query tile at a time: lane holds key column kloc and
     // query rows {8a + 4h + r}
 #pragma unroll
-    for (int qt = 0; qt < C::T32; ++qt) {
+    for (int qt = 0; qt < C::KC; ++qt) {
       floatx16 s, dp;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
-#pragma unroll
-      for (int ds = 0; ds < C::DS; ++ds) {
-        const bf16x8 qa = read_row8<C::CPR>(qs, qt * 32 + l32, ds * 2 + hf);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
-        const bf16x8 ga = read_row8<C::CPR>(gs, qt * 32 + l32, ds * 2 + hf);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ds], dp, 0, 0, 0);
-      }
+      two_products<D>(qs, gs, kf, vf, s, dp, qt * 32, l32, hf);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int qr = i * BS + qt * 32 + 8 * g + 4 * hf;       // 4 consecutive query rows
-        const float4 l4 = *reinterpret_cast<const float4*>(lse2h + qr);
-        const float4 d4 = *reinterpret_cast<const float4*>(delh + qr);
+        const int qr = qt * 32 + 8 * g + 4 * hf;       // 4 consecutive query rows of the unit
+        const float4 l4 = *reinterpret_cast<const float4*>(ls + qr);
+        const float4 d4 = *reinterpret_cast<const float4*>(ls + C::SUB + qr);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -439,24 +529,36 @@ __global__ __launch_bounds__(2 * BS, 1) void dkv_kernel(
       }
       const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 1);
       const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 1);
+      // step st: d tile st % DT, 16-query half (st / DT) & 1, dV (st < 2 DT) or
+      // dK; consecutive MFMAs update different accumulators
+      constexpr int NS = 4 * C::DT, AHEAD = 2;
+      auto rd = [&](int st) {
+        const char* t = st >= 2 * C::DT ? qs : gs;
+        return read_tr8<C::CPR>(t, qt * 32 + 16 * ((st / C::DT) & 1), (st % C::DT) * 32, lane);
+      };
+      bf16x8 a[NS];
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        bf16x8 a = read_tr8<C::CPR>(gs, qt * 32, dt * 32, lane);
-        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, adv[dt], 0, 0, 0);
-        a = read_tr8<C::CPR>(gs, qt * 32 + 16, dt * 32, lane);
-        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, adv[dt], 0, 0, 0);
-        a = read_tr8<C::CPR>(qs, qt * 32, dt * 32, lane);
-        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, d0, adk[dt], 0, 0, 0);
-        a = read_tr8<C::CPR>(qs, qt * 32 + 16, dt * 32, lane);
-        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, d1, adk[dt], 0, 0, 0);
+      for (int st = 0; st < AHEAD; ++st) a[st] = rd(st);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + AHEAD < NS) a[st + AHEAD] = rd(st + AHEAD);
+        const int dt = st % C::DT, half = (st / C::DT) & 1;
+        if (st >= 2 * C::DT)
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? d1 : d0, adk[dt], 0, 0, 0);
+        else
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? p1 : p0, adv[dt], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  for (int it = 0; it < n_e; it += 2) {
-    do_block(q0s, g0s, q1s, g1s, it);
-    if (it + 1 < n_e) do_block(q1s, g1s, q0s, g0s, it + 1);
+  int u = 0;
+  for (; u + 1 < n_u; u += 2) {
+    unit(u, q0s, g0s, ld0s, q1s, g1s, ld1s);
+    unit(u + 1, q1s, g1s, ld1s, q0s, g0s, ld0s);
   }
+  if (u < n_u) unit(u, q0s, g0s, ld0s, q1s, g1s, ld1s);
 
   if (kk < N) {
     __bf16* krow = dk + ((size_t)bh * N + kk) * D;
