@@ -15,6 +15,9 @@ What it computes, in the order the method runs:
   (logit descending, block index ascending) and keep the shortest prefix
   whose cumulative probability reaches p; blocks that hold prefix (text)
   tokens are added afterwards.
+* Mask narrowing: Top-p over the exact block attention weights of an earlier
+  step, restricted to that step's blocks (GSRS page, Abstract; Figure 4
+  caption) -- the same ranking and cut as the estimator, applied to masses.
 * Sparse attention over the selected key blocks, computed with whole rows
   (no online rescaling): O, the per-query log-sum-exp and the exact
   attention mass of every (query block, key block) pair -- the block-level
@@ -140,6 +143,85 @@ def selection_band(row: RowSelection, top_p: float, tol: float = 1e-4,
     for r in range(2, n + 1):
         if abs(row.cumulative[r - 2] - p) <= mass_tol:
             band.add(int(row.ranked[r - 1]))
+    return band - set(row.forced.tolist())
+
+
+def top_p_from_mass(entries: np.ndarray, mass: np.ndarray, top_p: float,
+                    forced: np.ndarray | None = None) -> RowSelection:
+    """Top-p over a row's exact block attention weights (mask narrowing).
+
+    The GSRS page (Abstract) evaluates exact attention weights inside the
+    attention computation and restricts later search steps to the blocks an
+    earlier step kept (Abstract; Figure 4 caption); its Figure 3 caption
+    describes the block-level map those weights form.  Narrowing applies the
+    same Top-p rule as ``top_p_select`` to those weights instead of to a
+    softmax of pooled scores: the row's entries are ranked by mass, larger
+    first, the lower block index first on equal masses, and k* is the smallest
+    r whose cumulative share C_r = (sum of the top r masses) / (row total)
+    reaches p.  A negative or NaN mass counts as 0; a row whose total is 0
+    keeps every entry (C_n never reaches p); a block listed twice counts once,
+    with its first mass.  Forced blocks join after the cut.  The result lists
+    ascending block ids.
+    """
+    ent = np.asarray(entries, dtype=np.int64)
+    m = np.asarray(mass, dtype=np.float64)
+    m = np.where(m > 0, m, 0.0)               # NaN > 0 is False
+    _, first = np.unique(ent, return_index=True)
+    first = np.sort(first)
+    ent, m = ent[first], m[first]
+    forced = np.zeros(0, dtype=np.int64) if forced is None else np.asarray(forced, dtype=np.int64)
+    n = ent.size
+    if n == 0:
+        return RowSelection(ent, m, ent, np.zeros(0), 0, forced, np.unique(forced))
+    order = np.lexsort((ent, -m))             # primary: -mass, secondary: id
+    ranked = ent[order]
+    total = m.sum()
+    p = float(top_p)
+    if total <= 0.0:
+        cum = np.zeros(n)
+        k_star = n
+    else:
+        cum = np.cumsum(m[order]) / total
+        if p >= 1.0:
+            k_star = n
+        else:
+            hit = np.nonzero(cum >= p)[0]
+            k_star = int(hit[0]) + 1 if hit.size else n
+    sel = np.union1d(ranked[:k_star], forced).astype(np.int64)
+    return RowSelection(ent, m, ranked, cum, k_star, forced, sel)
+
+
+def narrow_by_mass(row_ptr: np.ndarray, col_idx: np.ndarray, mass: np.ndarray, top_p: float,
+                   keep_prefix_tokens: int, block: int, nb: int):
+    """Narrow a CSR mask with ``top_p_from_mass`` row by row.
+
+    ``mass`` is aligned with ``col_idx`` (the forward's block mass).  Returns
+    (row_ptr, col_idx, selections).  Entry ids outside [0, nb) are ignored.
+    """
+    forced = forced_blocks(keep_prefix_tokens, block, nb)
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    ms = np.asarray(mass, dtype=np.float64)
+    sels = []
+    for r in range(rp.size - 1):
+        ent, m = ci[rp[r]:rp[r + 1]], ms[rp[r]:rp[r + 1]]
+        ok = (ent >= 0) & (ent < nb)
+        sels.append(top_p_from_mass(ent[ok], m[ok], top_p, forced))
+    out_rp, out_ci = rows_to_csr([s.selected for s in sels])
+    return out_rp, out_ci, sels
+
+
+def mass_band(row: RowSelection, top_p: float, mass_tol: float = 1e-5) -> set[int]:
+    """Blocks whose narrowing a rounding-level change of the cumulative share
+    could flip: rank r >= 2 with |C_{r-1} - p| <= mass_tol.  The masses
+    themselves are the same float32 values on both sides, so the ranking is
+    exact; only the summation order differs (float32 on the GPU).
+    """
+    n = row.ranked.size
+    if n == 0 or float(top_p) >= 1.0 or row.cumulative.size == 0 or row.cumulative[-1] == 0.0:
+        return set()
+    p = float(top_p)
+    band = {int(row.ranked[r - 1]) for r in range(2, n + 1) if abs(row.cumulative[r - 2] - p) <= mass_tol}
     return band - set(row.forced.tolist())
 
 

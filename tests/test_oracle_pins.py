@@ -176,6 +176,91 @@ def test_candidate_restriction():
 # pooling
 # ----------------------------------------------------------------------------
 
+# ----------------------------------------------------------------------------
+# mask narrowing: Top-p over exact block masses
+# ----------------------------------------------------------------------------
+
+def test_mass_top_p_hand_worked_fixture():
+    rows = [ln for ln in open(os.path.join(GOLDEN, "mass_top_p_hand_worked.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 12
+    for ln in rows:
+        ent, masses, p, forced, expect = ln.split("|")
+        ent = np.array(_ints(ent), dtype=np.int64)
+        m = np.array([float(t) for t in masses.split()] if masses.strip() != "-" else [], dtype=np.float64)
+        sel = O.top_p_from_mass(ent, m, float(p), np.array(_ints(forced), dtype=np.int64))
+        assert sel.selected.tolist() == _ints(expect), ln
+
+
+def _brute_force_mass(m, p):
+    """Smallest subset whose share of the total reaches p; then largest mass; then lowest ids."""
+    n = len(m)
+    z = sum(m)
+    for size in range(1, n + 1):
+        best = None
+        for sub in itertools.combinations(range(n), size):
+            s = sum(m[j] for j in sub) / z
+            if s >= p and (best is None or s > best[0] + 1e-12):
+                best = (s, sub)
+        if best is not None:
+            return sorted(best[1])
+    return list(range(n))
+
+
+def test_mass_top_p_brute_force_small_rows():
+    rng = np.random.default_rng(21)
+    checked = 0
+    while checked < 200:
+        n = int(rng.integers(1, 10))
+        m = rng.dirichlet(np.full(n, 0.7)) * float(rng.uniform(0.5, 2.0))
+        p = float(rng.uniform(0.05, 0.99))
+        shares = [x / m.sum() for x in m]
+        if _subset_margin(shares, p) < 1e-9:
+            continue
+        ent = np.sort(rng.choice(64, n, replace=False))
+        expect = ent[_brute_force_mass(m.tolist(), p)].tolist()
+        got = O.top_p_from_mass(ent, m, p)
+        assert got.selected.tolist() == expect
+        checked += 1
+
+
+def test_mass_top_p_equals_estimator_rule_on_softmax_weights():
+    # Masses equal to the softmax of some logits must select what the
+    # estimator's rule selects from those logits (two independent code paths:
+    # exp/normalise there, given shares here).
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        n = int(rng.integers(1, 120))
+        logits = rng.normal(0, 2.5, n)
+        p = float(rng.uniform(0.1, 0.99))
+        ent = np.sort(rng.choice(4096, n, replace=False))
+        a = O.top_p_select(ent, logits, p)
+        w = np.exp(logits - logits.max())
+        b = O.top_p_from_mass(ent, w / w.sum(), p)
+        band = O.selection_band(a, p, tol=1e-9, mass_tol=1e-9)
+        assert set(a.selected.tolist()) ^ set(b.selected.tolist()) <= band
+
+
+def test_narrow_by_mass_on_forward_masses():
+    # The forward's exact masses narrow a mask to a subset; p = 1 keeps it.
+    rng = np.random.default_rng(23)
+    B, H, N, D, bs = 1, 2, 700, 64, 64
+    nb = O.num_blocks(N, bs)
+    Q, K, V = (rng.normal(size=(B, H, N, D)) for _ in range(3))
+    rp, ci = _random_mask(rng, B, H, nb, empty_rows=True)
+    _, _, mass = O.sparse_forward(Q, K, V, bs, rp, ci, 0.125)
+    rp1, ci1, _ = O.narrow_by_mass(rp, ci, mass, 1.0, 0, bs, nb)
+    assert rp1.tolist() == list(rp) and ci1.tolist() == list(ci)
+    rp2, ci2, sels = O.narrow_by_mass(rp, ci, mass, 0.8, 0, bs, nb)
+    for r in range(rp.size - 1):
+        before = set(ci[rp[r]:rp[r + 1]].tolist())
+        after = set(ci2[rp2[r]:rp2[r + 1]].tolist())
+        assert after <= before
+        if before:
+            kept = sum(mass[rp[r] + sorted(before).index(j)] for j in after)
+            assert kept >= 0.8 * mass[rp[r]:rp[r + 1]].sum() - 1e-12
+
+
 def test_pool_blocks_matches_loop_on_ragged_tail():
     rng = np.random.default_rng(6)
     x = rng.normal(size=(37, 3))
