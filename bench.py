@@ -186,6 +186,25 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # Mask narrowing from the forward's exact block mass (reduced search of a
+    # later step): timed on its own, outside the step, at the next step's
+    # threshold (the same one for single-step workloads).
+    p_next = float(np.float32(w.top_p[1] if len(w.top_p) > 1 else w.top_p[0]))
+    narrowed = bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int32,
+                                                                                       device=dev))
+    ws_s = torch.empty(bsa.bsa_workspace_size(shape, 3, 0), dtype=torch.uint8, device=dev)
+    nsel = 10
+    bsa.bsa_select_from_mass(q, mask, mass, p_next, w.block, w.keep_prefix_tokens, out=narrowed, workspace=ws_s)
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(nsel):
+        bsa.bsa_select_from_mass(q, mask, mass, p_next, w.block, w.keep_prefix_tokens, out=narrowed, workspace=ws_s)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    sel_ms = s0.elapsed_time(s1) / nsel
+    nnz_narrow = int(narrowed.row_ptr[-1].item())
+
     rp, ci = mask.to_host()
     nnz = int(rp[-1])
     pairs = executed_pairs(w.N, w.block, w.B * w.H, rp, ci)
@@ -228,6 +247,10 @@ def main(argv=None) -> int:
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": "fwd_kernel"},
     }
+    sel_bytes = 4.0 * (R + 1) + 8.0 * nnz + 4.0 * (R + 1) + 4.0 * nnz_narrow
+    out["select_from_mass"] = {"ms": round(sel_ms, 4), "top_p": p_next, "entries_in": nnz, "entries_out": nnz_narrow,
+                               "algorithmic_bytes": sel_bytes,
+                               "gbps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1)}
     if w.backward:
         out["bwd_ms"] = round(bwd_ms, 4)
         out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)

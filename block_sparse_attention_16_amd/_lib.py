@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "bsa.h")
 
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
 BSA_BF16, BSA_FP32 = 0, 1
-BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_BACKWARD = 0, 1, 2
+BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_BACKWARD, BSA_WS_SELECT_FROM_MASS = 0, 1, 2, 3
 
 
 class BsaShape(ctypes.Structure):
@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
     L.bsa_workspace_size.restype = sz
     L.bsa_estimate_mask.argtypes = [P(BsaShape), vp, vp, f32, f32, P(BsaCsr), i32, P(BsaCsr), vp, sz, vp]
     L.bsa_estimate_mask.restype = i32
+    L.bsa_select_from_mass.argtypes = [P(BsaShape), P(BsaCsr), vp, f32, i32, P(BsaCsr), vp, sz, vp]
+    L.bsa_select_from_mass.restype = i32
     L.bsa_forward.argtypes = [P(BsaShape), vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
     L.bsa_forward.restype = i32
     L.bsa_backward.argtypes = [P(BsaShape), vp, vp, vp, vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]

@@ -12,7 +12,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_FORWARD, BsaCsr, BsaShape,
+from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_SELECT_FROM_MASS,
+                   BsaCsr, BsaShape,
                    check, load)
 
 
@@ -122,6 +123,30 @@ def bsa_estimate_mask(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int
     st = load().bsa_estimate_mask(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p), float(scale), cand,
                                   int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(), _stream())
     check(st, "bsa_estimate_mask")
+    return out
+
+
+def bsa_select_from_mass(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: float, block: int,
+                         keep_prefix_tokens: int = 0, out: Csr | None = None,
+                         workspace: torch.Tensor | None = None) -> Csr:
+    """Mask narrowing: Top-p over the block masses aligned with ``mask`` -> CSR
+    (see bsa_select_from_mass in include/bsa.h).  ``q`` supplies the shape only."""
+    _check(q, "q")
+    _check(mass, "mass", dtype=torch.float32)
+    if mass.numel() < mask.capacity:
+        raise ValueError("mass must hold mask.capacity entries")
+    shape = _shape_of(q, block)
+    nb = -(-q.shape[2] // block)
+    R = num_rows(q, block)
+    if out is None:
+        out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
+                  torch.empty(R * nb, dtype=torch.int32, device=q.device))
+    ws = _workspace(shape, BSA_WS_SELECT_FROM_MASS, 0, workspace, q.device)
+    mc, oc = mask.c(), out.c()
+    st = load().bsa_select_from_mass(ctypes.byref(shape), ctypes.byref(mc), mass.data_ptr(), float(top_p),
+                                     int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(),
+                                     _stream())
+    check(st, "bsa_select_from_mass")
     return out
 
 

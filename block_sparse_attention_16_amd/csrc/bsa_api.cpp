@@ -85,6 +85,7 @@ size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity
     case BSA_WS_ESTIMATE: bsa::carve_estimate(p, nullptr, &bytes); break;
     case BSA_WS_FORWARD: bsa::carve_forward(p, capacity, true, nullptr, &bytes); break;
     case BSA_WS_BACKWARD: bsa::carve_backward(p, capacity, nullptr, &bytes); break;
+    case BSA_WS_SELECT_FROM_MASS: bsa::carve_select(p, nullptr, &bytes); break;
     default: return 0;
   }
   return bytes;
@@ -116,6 +117,29 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
   return hip_status(bsa::launch_estimate(p, q, k, top_p, resolve_scale(scale, p.D), candidate, keep_prefix_tokens,
                                          out, w, static_cast<hipStream_t>(stream)),
                     "estimate launch");
+}
+
+bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass, float top_p,
+                                int32_t keep_prefix_tokens, bsa_csr* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  bsa::Problem p;
+  BSA_TRY(make_problem(shape, &p));
+  BSA_TRY(check_csr(mask, "mask"));
+  BSA_TRY(check_csr(out, "out"));
+  if (mask->capacity > 0 && !block_mass) return fail(BSA_ERR_INVALID_ARG, "block_mass is NULL");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(BSA_ERR_INVALID_ARG, "top_p=%g is outside (0, 1]", top_p);
+  if (keep_prefix_tokens < 0 || keep_prefix_tokens > p.N)
+    return fail(BSA_ERR_INVALID_ARG, "keep_prefix_tokens=%d is outside [0, N]", keep_prefix_tokens);
+  if (mask->row_ptr == out->row_ptr || (mask->col_idx && mask->col_idx == out->col_idx))
+    return fail(BSA_ERR_INVALID_ARG, "mask aliases out");
+  size_t need = 0;
+  bsa::carve_select(p, nullptr, &need);
+  if (ws_bytes < need || (need && !ws))
+    return fail(BSA_ERR_WORKSPACE, "select workspace needs %zu bytes, got %zu", need, ws_bytes);
+  bsa::SelectWs w = bsa::carve_select(p, ws, &need);
+  return hip_status(bsa::launch_select_from_mass(p, mask, block_mass, top_p, keep_prefix_tokens, out, w,
+                                                 static_cast<hipStream_t>(stream)),
+                    "select-from-mass launch");
 }
 
 bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v, float scale,

@@ -46,6 +46,16 @@ hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float
                            const bsa_csr* cand, int keep_prefix_tokens, const bsa_csr* out,
                            const EstimateWs& w, hipStream_t s);
 
+// ---- mask narrowing from block masses (estimate.hip) ----
+struct SelectWs {
+  int32_t* counts;   // [R] kept entries per row
+  uint32_t* bits;    // [R, words] kept-block bitmask
+  int words;
+};
+SelectWs carve_select(const Problem& p, void* ws, size_t* bytes);
+hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const float* mass, float top_p,
+                                   int keep_prefix_tokens, const bsa_csr* out, const SelectWs& w, hipStream_t s);
+
 // ---- forward (forward_bf16.hip, forward_fp32.hip) ----
 struct ForwardWs {
   float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)

@@ -16,6 +16,11 @@
 //                   forced prefix blocks -> selection bitmask
 //   scan_kernel     exclusive scan of the per-row counts -> CSR row_ptr
 //   compact_kernel  one wavefront per row: bitmask -> ascending col_idx
+//
+// Mask narrowing (GSRS page, Abstract and Figure 4 caption: exact attention
+// weights, later searches restricted to an earlier step's blocks) reuses
+// select_kernel in its FROM_MASS form -- the weights are a CSR row's block
+// masses instead of exp(logit - max) -- followed by the same scan and compact.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -158,7 +163,12 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 // kept and blocks exactly at L* are added in ascending id until the mass
 // reaches p * Z.  This is the shortest prefix of the (logit desc, id asc)
 // ranking whose cumulative probability reaches p, summed in another order.
-template <int EPL>
+//
+// FROM_MASS: `logits` is a [capacity] array of block masses aligned with
+// cand_idx (cand_ptr is required); the weight of a block is its mass (a
+// negative or NaN mass counts as 0) and ranking is by mass.  A row whose
+// masses sum to 0 keeps every entry.
+template <int EPL, bool FROM_MASS>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ logits, int nb, int R, float top_p, const int32_t* __restrict__ cand_ptr,
     const int32_t* __restrict__ cand_idx, int64_t cand_cap, int n_forced, int32_t* __restrict__ counts,
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   } else {
     n_c = nb;
   }
-  const float* lrow = logits + (size_t)r * nb;
+  const float* lrow = FROM_MASS ? logits + lo : logits + (size_t)r * nb;
   uint32_t key[EPL];
   int jj[EPL];
   float sv[EPL];
@@ -202,7 +212,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         bool fresh = true;
         if (cand_ptr) fresh = (atomicOr(&my_seen[j >> 5], 1u << (j & 31)) & (1u << (j & 31))) == 0u;
         if (fresh) {
-          sv[e] = lrow[j];
+          if constexpr (FROM_MASS) {
+            const float m = lrow[t];
+            sv[e] = m > 0.f ? m : 0.f;       // NaN compares false
+          } else {
+            sv[e] = lrow[j];
+          }
           key[e] = ordered_bits(sv[e]);
           jj[e] = j;
           kmax = max(kmax, key[e]);
@@ -217,13 +232,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   float zl = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    ev[e] = key[e] ? expf(sv[e] - smax) : 0.f;
+    if constexpr (FROM_MASS) ev[e] = sv[e];
+    else ev[e] = key[e] ? expf(sv[e] - smax) : 0.f;
     zl += ev[e];
   }
   const float Z = wave_sum(zl);
   uint32_t cut = 1u;                         // keep every present block by default
   bool tie_walk = false;
-  if (top_p < 1.0f && kmax != 0u) {
+  if (top_p < 1.0f && kmax != 0u && Z > 0.f) {
     const float thr = top_p * Z;
     uint32_t T = 0u;
     for (int bit = 31; bit >= 0; --bit) {
@@ -373,12 +389,27 @@ static void launch_pool_logits(const Problem& p, const void* q, const void* k, f
   logits_kernel<D><<<g, kThreads, 0, s>>>(w.qbar, w.kbar, w.logits, p.nb, scale);
 }
 
-template <int EPL>
-static void launch_select(const Problem& p, float top_p, const bsa_csr* cand, int n_forced, const EstimateWs& w,
-                          hipStream_t s) {
-  select_kernel<EPL><<<(p.R + 3) / 4, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, cand ? cand->row_ptr : nullptr,
-                                                        cand ? cand->col_idx : nullptr, cand ? cand->capacity : 0,
-                                                        n_forced, w.counts, w.bits, w.words);
+template <int EPL, bool FROM_MASS>
+static void launch_select(const Problem& p, const float* vals, float top_p, const bsa_csr* cand, int n_forced,
+                          int32_t* counts, uint32_t* bits, int words, hipStream_t s) {
+  select_kernel<EPL, FROM_MASS><<<(p.R + 3) / 4, kThreads, 0, s>>>(
+      vals, p.nb, p.R, top_p, cand ? cand->row_ptr : nullptr, cand ? cand->col_idx : nullptr,
+      cand ? cand->capacity : 0, n_forced, counts, bits, words);
+}
+
+template <bool FROM_MASS>
+static void launch_select_any(const Problem& p, const float* vals, float top_p, const bsa_csr* cand, int n_forced,
+                              int32_t* counts, uint32_t* bits, int words, hipStream_t s) {
+  if (p.nb <= 64) launch_select<1, FROM_MASS>(p, vals, top_p, cand, n_forced, counts, bits, words, s);
+  else if (p.nb <= 256) launch_select<4, FROM_MASS>(p, vals, top_p, cand, n_forced, counts, bits, words, s);
+  else if (p.nb <= 1024) launch_select<16, FROM_MASS>(p, vals, top_p, cand, n_forced, counts, bits, words, s);
+  else launch_select<64, FROM_MASS>(p, vals, top_p, cand, n_forced, counts, bits, words, s);
+}
+
+static void launch_csr(const Problem& p, const int32_t* counts, const uint32_t* bits, int words, const bsa_csr* out,
+                       hipStream_t s) {
+  scan_kernel<<<1, 1024, 0, s>>>(counts, out->row_ptr, p.R);
+  compact_kernel<<<(p.R + 3) / 4, kThreads, 0, s>>>(bits, out->row_ptr, out->col_idx, out->capacity, p.R, words);
 }
 
 hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
@@ -393,13 +424,26 @@ hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float
     if (bf) launch_pool_logits<__bf16, 128>(p, q, k, scale, w, s);
     else launch_pool_logits<float, 128>(p, q, k, scale, w, s);
   }
-  if (p.nb <= 64) launch_select<1>(p, top_p, cand, n_forced, w, s);
-  else if (p.nb <= 256) launch_select<4>(p, top_p, cand, n_forced, w, s);
-  else if (p.nb <= 1024) launch_select<16>(p, top_p, cand, n_forced, w, s);
-  else launch_select<64>(p, top_p, cand, n_forced, w, s);
-  scan_kernel<<<1, 1024, 0, s>>>(w.counts, out->row_ptr, p.R);
-  compact_kernel<<<(p.R + 3) / 4, kThreads, 0, s>>>(w.bits, out->row_ptr, out->col_idx, out->capacity, p.R,
-                                                    w.words);
+  launch_select_any<false>(p, w.logits, top_p, cand, n_forced, w.counts, w.bits, w.words, s);
+  launch_csr(p, w.counts, w.bits, w.words, out, s);
+  return hipGetLastError();
+}
+
+SelectWs carve_select(const Problem& p, void* ws, size_t* bytes) {
+  Carver c(ws);
+  SelectWs w;
+  w.words = (p.nb + 31) / 32;
+  w.counts = c.take<int32_t>((size_t)p.R);
+  w.bits = c.take<uint32_t>((size_t)p.R * w.words);
+  *bytes = align_up(c.off, 256);
+  return w;
+}
+
+hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const float* mass, float top_p,
+                                   int keep_prefix_tokens, const bsa_csr* out, const SelectWs& w, hipStream_t s) {
+  const int n_forced = min(p.nb, (keep_prefix_tokens + p.bs - 1) / p.bs);
+  launch_select_any<true>(p, mass, top_p, mask, n_forced, w.counts, w.bits, w.words, s);
+  launch_csr(p, w.counts, w.bits, w.words, out, s);
   return hipGetLastError();
 }
 

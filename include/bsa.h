@@ -78,7 +78,12 @@ typedef struct {
 } bsa_csr;
 
 /* Which call a workspace is sized for. */
-typedef enum { BSA_WS_ESTIMATE = 0, BSA_WS_FORWARD = 1, BSA_WS_BACKWARD = 2 } bsa_ws_kind;
+typedef enum {
+  BSA_WS_ESTIMATE = 0,
+  BSA_WS_FORWARD = 1,
+  BSA_WS_BACKWARD = 2,
+  BSA_WS_SELECT_FROM_MASS = 3
+} bsa_ws_kind;
 
 /* Bytes of device workspace `kind` needs for `shape` and a CSR of `capacity`
  * entries (the forward stores per-entry partial sums for the block mass).
@@ -107,6 +112,31 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
                              float top_p, float scale, const bsa_csr* candidate,
                              int32_t keep_prefix_tokens, bsa_csr* out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Mask narrowing from exact block attention weights.  The GSRS page
+ * (Abstract) obtains exact attention weights inside the attention computation
+ * and restricts later search steps to the blocks of an earlier step
+ * (Abstract; Figure 4 caption); its Figure 3 caption describes the
+ * block-level attention map those weights form.  This call applies the
+ * estimator's Top-p rule to such weights: row r of `mask` is ranked by the
+ * block masses aligned with it (larger first, lower block id first on equal
+ * masses) and keeps the shortest prefix whose share of the row's total mass
+ * reaches top_p; forced blocks (keep_prefix_tokens, as in bsa_estimate_mask)
+ * join after the cut.
+ *   mask       CSR over the R rows, e.g. the one a forward ran on.
+ *   block_mass [mask->capacity] fp32 device array aligned with mask->col_idx,
+ *              e.g. bsa_forward's block_mass.  A negative or NaN mass counts
+ *              as 0; a row whose masses sum to 0 keeps every entry; a block
+ *              listed twice in a row counts once, with its first mass.
+ *   top_p      in (0, 1]; 1 keeps every entry.
+ *   out        CSR written by the call (a subset of mask plus forced blocks),
+ *              rows ascending; exact row_ptr offsets, entries past
+ *              out->capacity dropped, as in bsa_estimate_mask.  Must not alias
+ *              mask.
+ *   ws         at least bsa_workspace_size(shape, BSA_WS_SELECT_FROM_MASS, 0) bytes. */
+bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass,
+                                float top_p, int32_t keep_prefix_tokens, bsa_csr* out,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Sparse attention forward over a block mask (see the header comment, stage 2).
  *   q, k, v    [B,H,N,D] device tensors of shape->dtype.

@@ -27,7 +27,7 @@ def _csr(cap=1024):
 def test_library_exports_every_header_function():
     names = _lib.header_functions()
     assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error",
-                            "bsa_status_string", "bsa_version", "bsa_workspace_size"])
+                            "bsa_select_from_mass", "bsa_status_string", "bsa_version", "bsa_workspace_size"])
     L = _lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -53,6 +53,8 @@ def test_workspace_sizes():
     assert est >= 2 * R * D * 4 + R * 4 + R * 4
     fwd = L.bsa_workspace_size(ctypes.byref(s), 1, 100)
     assert fwd >= 100 * 64 * 4          # per-entry, per-query partial sums for the block mass
+    sel = L.bsa_workspace_size(ctypes.byref(s), 3, 0)
+    assert sel >= R * 4 + R * ((nb + 31) // 32) * 4      # counts + kept-block bitmask
     assert L.bsa_workspace_size(ctypes.byref(_shape(D=96)), 0, 0) == 0
     assert L.bsa_workspace_size(ctypes.byref(s), 7, 0) == 0
 
@@ -109,6 +111,28 @@ def test_forward_and_backward_validation():
     st = L.bsa_backward(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, ctypes.byref(m), FAKE,
                         FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == _lib.BSA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_select_from_mass_validation():
+    L = _lib.load()
+    s = _shape()
+    m, o = _csr(), _lib.BsaCsr(FAKE + 8192, FAKE + 16384, 1024)
+
+    def call(shape=s, mask=m, mass=FAKE, p=0.9, keep=0, out=o, ws=FAKE, ws_bytes=1 << 30):
+        return L.bsa_select_from_mass(ctypes.byref(shape), ctypes.byref(mask) if mask else None, mass, p, keep,
+                                      ctypes.byref(out) if out else None, ws, ws_bytes, None)
+
+    assert call(mass=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(mask=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(out=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(p=0.0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(p=1.01) == _lib.BSA_ERR_INVALID_ARG
+    assert call(p=float("nan")) == _lib.BSA_ERR_INVALID_ARG
+    assert call(keep=-3) == _lib.BSA_ERR_INVALID_ARG
+    assert call(out=m) == _lib.BSA_ERR_INVALID_ARG                     # mask aliases out
+    assert call(ws_bytes=8) == _lib.BSA_ERR_WORKSPACE
+    assert call(shape=_shape(block=96)) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
