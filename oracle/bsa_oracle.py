@@ -18,6 +18,9 @@ What it computes, in the order the method runs:
 * Mask narrowing: Top-p over the exact block attention weights of an earlier
   step, restricted to that step's blocks (GSRS page, Abstract; Figure 4
   caption) -- the same ranking and cut as the estimator, applied to masses.
+* Structured head masks: the SVG page's spatial and temporal heads and the
+  Sparse-vDiT page's diagonal, multi-diagonal and vertical-stripe patterns
+  (both Abstracts), lifted from token pairs to block pairs.
 * Sparse attention over the selected key blocks, computed with whole rows
   (no online rescaling): O, the per-query log-sum-exp and the exact
   attention mass of every (query block, key block) pair -- the block-level
@@ -281,6 +284,81 @@ def estimate_mask(Q: np.ndarray, K: np.ndarray, block: int, top_p: float, scale:
         all_rows.extend(r.selected for r in rs)
     row_ptr, col_idx = rows_to_csr(all_rows)
     return row_ptr, col_idx, sels
+
+
+# ----------------------------------------------------------------------------
+# structured (static) head masks
+# ----------------------------------------------------------------------------
+
+# Head kinds of the structured-mask generator.
+PATTERN_DENSE, PATTERN_SPATIAL, PATTERN_TEMPORAL, PATTERN_DIAGONAL, PATTERN_MULTI_DIAGONAL, PATTERN_STRIPES = range(6)
+
+
+def _block_tokens(i: int, block: int, N: int) -> range:
+    return range(i * block, min((i + 1) * block, N))
+
+
+def structured_block_mask(kind: int, N: int, block: int, prefix: int, frame_tokens: int, band: int,
+                          period: int, stripes=()) -> np.ndarray:
+    """Block-level mask [nb, nb] of one head for a structured pattern.
+
+    Token geometry: tokens [0, prefix) are text; a video token n >= prefix sits
+    in frame (n - prefix) // F at spatial index (n - prefix) % F, F =
+    frame_tokens.  Patterns:
+      spatial  (SVG page, Abstract: Spatial Head) -- a video query token
+               attends to the video key tokens of its own frame;
+      temporal (SVG page, Abstract: Temporal Head) -- to the video key tokens
+               at its own spatial index in every frame;
+      diagonal / multi-diagonal / vertical-stripe (Sparse-vDiT page,
+               Abstract) -- block bands |i - j| <= band; bands around every
+               multiple of `period` blocks, |i - j - k period| <= band; the
+               listed key blocks for every row plus the band |i - j| <= band;
+      dense    -- every pair.
+    Every pattern also keeps text: pairs with a text query or text key token
+    are related.  A block pair (i, j) is kept iff some token pair of it is
+    related (for the block patterns, iff the block relation holds or a text
+    token is involved).
+    """
+    nb = num_blocks(N, block)
+    rel = np.zeros((nb, nb), dtype=bool)
+    F = max(1, int(frame_tokens))
+    stripes = set(int(j) for j in stripes)
+    toks = [_block_tokens(i, block, N) for i in range(nb)]
+    has_text = [any(n < prefix for n in t) for t in toks]
+    frames = [{(n - prefix) // F for n in t if n >= prefix} for t in toks]
+    spots = [{(n - prefix) % F for n in t if n >= prefix} for t in toks]
+    for i in range(nb):
+        for j in range(nb):
+            if has_text[i] or has_text[j] or kind == PATTERN_DENSE:
+                ok = True
+            elif kind == PATTERN_SPATIAL:
+                ok = bool(frames[i] & frames[j])
+            elif kind == PATTERN_TEMPORAL:
+                ok = bool(spots[i] & spots[j])
+            elif kind == PATTERN_DIAGONAL:
+                ok = abs(i - j) <= band
+            elif kind == PATTERN_MULTI_DIAGONAL:
+                ok = any(abs(i - j - k * period) <= band for k in range(-nb, nb + 1))
+            elif kind == PATTERN_STRIPES:
+                ok = j in stripes or abs(i - j) <= band
+            else:
+                raise ValueError(f"unknown pattern {kind}")
+            rel[i, j] = ok
+    return rel
+
+
+def structured_mask(B: int, H: int, N: int, block: int, kinds, prefix: int, frame_tokens: int, band: int,
+                    period: int, stripes=()):
+    """CSR over rows (b, h, i) with head (b, h) using pattern kinds[b*H + h]."""
+    rows = []
+    cache = {}
+    for bh in range(B * H):
+        kind = int(kinds[bh])
+        if kind not in cache:
+            cache[kind] = structured_block_mask(kind, N, block, prefix, frame_tokens, band, period, stripes)
+        m = cache[kind]
+        rows.extend(np.nonzero(m[i])[0].astype(np.int64) for i in range(m.shape[0]))
+    return rows_to_csr(rows)
 
 
 # ----------------------------------------------------------------------------

@@ -261,6 +261,68 @@ def test_narrow_by_mass_on_forward_masses():
             assert kept >= 0.8 * mass[rp[r]:rp[r + 1]].sum() - 1e-12
 
 
+# ----------------------------------------------------------------------------
+# structured head masks
+# ----------------------------------------------------------------------------
+
+def _token_relation(kind, N, prefix, F, block, band, period, stripes):
+    """Explicit N x N token relation (pattern definitions on token pairs), lifted
+    to blocks by 'any pair related'; block patterns use block ids of tokens."""
+    n = np.arange(N)
+    text = n < prefix
+    frame = np.where(text, -1, (n - prefix) // F)
+    spot = np.where(text, -1, (n - prefix) % F)
+    blk = n // block
+    dq, dk = np.meshgrid(blk, blk, indexing="ij")
+    d = dq - dk
+    if kind == O.PATTERN_DENSE:
+        tok = np.ones((N, N), dtype=bool)
+    elif kind == O.PATTERN_SPATIAL:
+        tok = frame[:, None] == frame[None, :]
+    elif kind == O.PATTERN_TEMPORAL:
+        tok = spot[:, None] == spot[None, :]
+    elif kind == O.PATTERN_DIAGONAL:
+        tok = np.abs(d) <= band
+    elif kind == O.PATTERN_MULTI_DIAGONAL:
+        r = np.mod(d, period)
+        tok = np.minimum(r, period - r) <= band
+    else:
+        tok = np.isin(dk, list(stripes)) | (np.abs(d) <= band)
+    tok = tok | text[:, None] | text[None, :]
+    nb = O.num_blocks(N, block)
+    out = np.zeros((nb, nb), dtype=bool)
+    np.logical_or.at(out, (dq.ravel(), dk.ravel()), tok.ravel())
+    return out
+
+
+@pytest.mark.parametrize("kind", range(6))
+def test_structured_mask_equals_token_level_lifting(kind):
+    for N, prefix, F, block, band, period in [(700, 30, 50, 64, 1, 3), (1000, 0, 96, 64, 0, 4),
+                                              (513, 200, 31, 128, 2, 2), (900, 77, 120, 64, 1, 5)]:
+        stripes = (0, 5, 9)
+        got = O.structured_block_mask(kind, N, block, prefix, F, band, period, stripes)
+        ref = _token_relation(kind, N, prefix, F, block, band, period, stripes)
+        assert (got == ref).all(), (kind, N, prefix, F, block)
+
+
+def test_structured_mask_special_cases():
+    N, bs = 1000, 64
+    nb = O.num_blocks(N, bs)
+    dense = np.ones((nb, nb), dtype=bool)
+    assert (O.structured_block_mask(O.PATTERN_SPATIAL, N, bs, 0, N, 0, 0) == dense).all()       # one frame
+    assert (O.structured_block_mask(O.PATTERN_TEMPORAL, N, bs, 0, 1, 0, 0) == dense).all()      # one position
+    assert (O.structured_block_mask(O.PATTERN_DIAGONAL, N, bs, 0, 10, nb, 0) == dense).all()
+    assert (O.structured_block_mask(O.PATTERN_MULTI_DIAGONAL, N, bs, 0, 10, 0, 1) == dense).all()
+    eye = O.structured_block_mask(O.PATTERN_STRIPES, N, bs, 0, 10, 0, 0, ())
+    assert (eye == np.eye(nb, dtype=bool)).all()
+    far = O.structured_block_mask(O.PATTERN_MULTI_DIAGONAL, N, bs, 0, 10, 1, 3 * nb)
+    assert (far == O.structured_block_mask(O.PATTERN_DIAGONAL, N, bs, 0, 10, 1, 0)).all()
+    for kind in (O.PATTERN_SPATIAL, O.PATTERN_TEMPORAL, O.PATTERN_DIAGONAL, O.PATTERN_MULTI_DIAGONAL):
+        m = O.structured_block_mask(kind, 1500, 64, 100, 130, 1, 4)
+        assert (m == m.T).all()
+        assert m[0].all() and m[:, 0].all()          # the text block is kept by and keeps everything
+
+
 def test_pool_blocks_matches_loop_on_ragged_tail():
     rng = np.random.default_rng(6)
     x = rng.normal(size=(37, 3))
