@@ -16,7 +16,9 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "bsa.h")
 
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
 BSA_BF16, BSA_FP32 = 0, 1
-BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_BACKWARD, BSA_WS_SELECT_FROM_MASS = 0, 1, 2, 3
+BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_BACKWARD, BSA_WS_SELECT_FROM_MASS, BSA_WS_STRUCTURED = 0, 1, 2, 3, 4
+(BSA_PATTERN_DENSE, BSA_PATTERN_SPATIAL, BSA_PATTERN_TEMPORAL, BSA_PATTERN_DIAGONAL, BSA_PATTERN_MULTI_DIAGONAL,
+ BSA_PATTERN_STRIPES) = range(6)
 
 
 class BsaShape(ctypes.Structure):
@@ -26,6 +28,11 @@ class BsaShape(ctypes.Structure):
 
 class BsaCsr(ctypes.Structure):
     _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
+class BsaPatternParams(ctypes.Structure):
+    _fields_ = [("prefix_tokens", ctypes.c_int32), ("frame_tokens", ctypes.c_int32), ("band", ctypes.c_int32),
+                ("period", ctypes.c_int32), ("stripes", ctypes.c_void_p), ("n_stripes", ctypes.c_int32)]
 
 
 class BsaError(RuntimeError):
@@ -53,6 +60,8 @@ def load() -> ctypes.CDLL:
     L.bsa_estimate_mask.restype = i32
     L.bsa_select_from_mass.argtypes = [P(BsaShape), P(BsaCsr), vp, f32, i32, P(BsaCsr), vp, sz, vp]
     L.bsa_select_from_mass.restype = i32
+    L.bsa_structured_mask.argtypes = [P(BsaShape), vp, P(BsaPatternParams), P(BsaCsr), vp, sz, vp]
+    L.bsa_structured_mask.restype = i32
     L.bsa_forward.argtypes = [P(BsaShape), vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
     L.bsa_forward.restype = i32
     L.bsa_backward.argtypes = [P(BsaShape), vp, vp, vp, vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]

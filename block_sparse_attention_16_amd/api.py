@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_SELECT_FROM_MASS,
-                   BsaCsr, BsaShape,
+                   BSA_WS_STRUCTURED, BsaCsr, BsaPatternParams, BsaShape,
                    check, load)
 
 
@@ -147,6 +147,37 @@ def bsa_select_from_mass(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: 
                                      int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(),
                                      _stream())
     check(st, "bsa_select_from_mass")
+    return out
+
+
+def bsa_structured_mask(q: torch.Tensor, head_kind: torch.Tensor, block: int, prefix_tokens: int = 0,
+                        frame_tokens: int = 1, band: int = 0, period: int = 1, stripes: torch.Tensor | None = None,
+                        out: Csr | None = None, workspace: torch.Tensor | None = None) -> Csr:
+    """Structured head masks -> CSR (see bsa_structured_mask in include/bsa.h).
+    ``q`` supplies the shape only; ``head_kind`` is an int32 device tensor of B*H pattern codes."""
+    _check(q, "q")
+    B, H, N, _ = q.shape
+    if head_kind.dtype != torch.int32 or head_kind.numel() != B * H or head_kind.device != q.device:
+        raise ValueError("head_kind must be an int32 tensor of B*H entries on q's device")
+    head_kind = head_kind.contiguous()
+    if stripes is not None:
+        if stripes.dtype != torch.int32 or stripes.device != q.device:
+            raise ValueError("stripes must be an int32 tensor on q's device")
+        stripes = stripes.contiguous()
+    shape = _shape_of(q, block)
+    nb = -(-N // block)
+    R = num_rows(q, block)
+    if out is None:
+        out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
+                  torch.empty(R * nb, dtype=torch.int32, device=q.device))
+    ws = _workspace(shape, BSA_WS_STRUCTURED, 0, workspace, q.device)
+    prm = BsaPatternParams(int(prefix_tokens), int(frame_tokens), int(band), int(period),
+                           stripes.data_ptr() if stripes is not None and stripes.numel() else None,
+                           int(stripes.numel()) if stripes is not None else 0)
+    oc = out.c()
+    st = load().bsa_structured_mask(ctypes.byref(shape), head_kind.data_ptr(), ctypes.byref(prm), ctypes.byref(oc),
+                                    ws.data_ptr(), ws.numel(), _stream())
+    check(st, "bsa_structured_mask")
     return out
 
 

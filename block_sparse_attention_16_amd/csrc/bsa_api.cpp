@@ -85,7 +85,8 @@ size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity
     case BSA_WS_ESTIMATE: bsa::carve_estimate(p, nullptr, &bytes); break;
     case BSA_WS_FORWARD: bsa::carve_forward(p, capacity, true, nullptr, &bytes); break;
     case BSA_WS_BACKWARD: bsa::carve_backward(p, capacity, nullptr, &bytes); break;
-    case BSA_WS_SELECT_FROM_MASS: bsa::carve_select(p, nullptr, &bytes); break;
+    case BSA_WS_SELECT_FROM_MASS:
+    case BSA_WS_STRUCTURED: bsa::carve_select(p, nullptr, &bytes); break;
     default: return 0;
   }
   return bytes;
@@ -140,6 +141,32 @@ bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, con
   return hip_status(bsa::launch_select_from_mass(p, mask, block_mass, top_p, keep_prefix_tokens, out, w,
                                                  static_cast<hipStream_t>(stream)),
                     "select-from-mass launch");
+}
+
+bsa_status bsa_structured_mask(const bsa_shape* shape, const int32_t* head_kind, const bsa_pattern_params* params,
+                               bsa_csr* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  bsa::Problem p;
+  BSA_TRY(make_problem(shape, &p));
+  if (!head_kind) return fail(BSA_ERR_INVALID_ARG, "head_kind is NULL");
+  if (!params) return fail(BSA_ERR_INVALID_ARG, "params is NULL");
+  BSA_TRY(check_csr(out, "out"));
+  const bsa_pattern_params& q = *params;
+  if (q.prefix_tokens < 0 || q.prefix_tokens > p.N)
+    return fail(BSA_ERR_INVALID_ARG, "prefix_tokens=%d is outside [0, N]", q.prefix_tokens);
+  if (q.frame_tokens < 1) return fail(BSA_ERR_INVALID_ARG, "frame_tokens=%d must be >= 1", q.frame_tokens);
+  if (q.band < 0) return fail(BSA_ERR_INVALID_ARG, "band=%d must be >= 0", q.band);
+  if (q.period < 1) return fail(BSA_ERR_INVALID_ARG, "period=%d must be >= 1", q.period);
+  if (q.n_stripes < 0 || (q.n_stripes > 0 && !q.stripes))
+    return fail(BSA_ERR_INVALID_ARG, "stripes: n_stripes=%d with %s array", q.n_stripes,
+                q.stripes ? "an" : "no");
+  size_t need = 0;
+  bsa::carve_select(p, nullptr, &need);
+  if (ws_bytes < need || (need && !ws))
+    return fail(BSA_ERR_WORKSPACE, "structured-mask workspace needs %zu bytes, got %zu", need, ws_bytes);
+  bsa::SelectWs w = bsa::carve_select(p, ws, &need);
+  return hip_status(bsa::launch_structured_mask(p, head_kind, q, out, w, static_cast<hipStream_t>(stream)),
+                    "structured-mask launch");
 }
 
 bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v, float scale,

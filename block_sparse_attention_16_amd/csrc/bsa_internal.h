@@ -56,6 +56,10 @@ SelectWs carve_select(const Problem& p, void* ws, size_t* bytes);
 hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const float* mass, float top_p,
                                    int keep_prefix_tokens, const bsa_csr* out, const SelectWs& w, hipStream_t s);
 
+// ---- structured head masks (estimate.hip); same workspace as narrowing ----
+hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, const bsa_pattern_params& prm,
+                                  const bsa_csr* out, const SelectWs& w, hipStream_t s);
+
 // ---- forward (forward_bf16.hip, forward_fp32.hip) ----
 struct ForwardWs {
   float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)

@@ -21,6 +21,12 @@
 // weights, later searches restricted to an earlier step's blocks) reuses
 // select_kernel in its FROM_MASS form -- the weights are a CSR row's block
 // masses instead of exp(logit - max) -- followed by the same scan and compact.
+//
+// Structured head masks (SVG page, Abstract: spatial and temporal heads;
+// Sparse-vDiT page, Abstract: diagonal, multi-diagonal and vertical-stripe
+// patterns): pattern_kernel evaluates the block relation of each row's head
+// with interval arithmetic on frames and spatial positions, into the same
+// bitmask, then the same scan and compact.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -365,6 +371,97 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const uint32_t* __res
   }
 }
 
+// Token range of block i and its video part, in the frame geometry of the
+// structured patterns (tokens [0, prefix) are text; video token n is at frame
+// (n - prefix) / F, spatial index (n - prefix) % F).
+struct BlockGeo {
+  int vlo, hi;     // video tokens [vlo, hi); empty when vlo >= hi
+  bool text;       // the block holds a text token
+};
+__device__ __forceinline__ BlockGeo block_geo(int i, int bs, int N, int prefix) {
+  const int lo = i * bs, hi = min(lo + bs, N);
+  return {max(lo, prefix), hi, lo < prefix};
+}
+// Spatial positions of a block's video tokens as up to two intervals.
+__device__ __forceinline__ int spot_intervals(const BlockGeo& g, int prefix, int F, int (&a)[2], int (&b)[2]) {
+  const int len = g.hi - g.vlo;
+  if (len >= F) { a[0] = 0; b[0] = F - 1; return 1; }
+  const int s0 = (g.vlo - prefix) % F, s1 = (g.hi - 1 - prefix) % F;
+  if (s0 <= s1) { a[0] = s0; b[0] = s1; return 1; }
+  a[0] = s0; b[0] = F - 1; a[1] = 0; b[1] = s1;
+  return 2;
+}
+
+// One wavefront per mask row: the row's key blocks under its head's pattern
+// -> selection bitmask and count.  Unknown kinds give dense rows.
+__global__ __launch_bounds__(kThreads) void pattern_kernel(const int32_t* __restrict__ head_kind, int nb, int R,
+                                                           int N, int bs, int prefix, int F, int band, int period,
+                                                           const int32_t* __restrict__ stripes, int n_stripes,
+                                                           int32_t* __restrict__ counts, uint32_t* __restrict__ bits,
+                                                           int words) {
+  __shared__ uint32_t stripe_bits[kSortMax / 32];
+  for (int w = threadIdx.x; w < words; w += kThreads) stripe_bits[w] = 0u;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n_stripes; t += kThreads) {
+    const int j = stripes[t];
+    if (j >= 0 && j < nb) atomicOr(&stripe_bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kThreads / 64) + wid;
+  if (r >= R) return;
+  const int i = r % nb;
+  const int kind = head_kind[r / nb];
+  const BlockGeo gi = block_geo(i, bs, N, prefix);
+  const bool vi = gi.vlo < gi.hi;
+  int ai[2], bi[2], ni = 0;
+  if (kind == BSA_PATTERN_TEMPORAL && vi) ni = spot_intervals(gi, prefix, F, ai, bi);
+  const int fi0 = vi ? (gi.vlo - prefix) / F : 0, fi1 = vi ? (gi.hi - 1 - prefix) / F : -1;
+  int cnt = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t word = 0u;
+    if (w < words) {
+      for (int b = 0; b < 32; ++b) {
+        const int j = w * 32 + b;
+        if (j >= nb) break;
+        const BlockGeo gj = block_geo(j, bs, N, prefix);
+        const bool vj = gj.vlo < gj.hi;
+        const int d = i - j;
+        bool keep;
+        if (gi.text || gj.text) {
+          keep = true;
+        } else if (kind == BSA_PATTERN_SPATIAL) {
+          const int fj0 = (gj.vlo - prefix) / F, fj1 = (gj.hi - 1 - prefix) / F;
+          keep = vi && vj && fi0 <= fj1 && fj0 <= fi1;
+        } else if (kind == BSA_PATTERN_TEMPORAL) {
+          keep = false;
+          if (vi && vj) {
+            int aj[2], bj[2];
+            const int nj = spot_intervals(gj, prefix, F, aj, bj);
+            for (int x = 0; x < ni; ++x)
+              for (int y = 0; y < nj; ++y) keep = keep || (ai[x] <= bj[y] && aj[y] <= bi[x]);
+          }
+        } else if (kind == BSA_PATTERN_DIAGONAL) {
+          keep = abs(d) <= band;
+        } else if (kind == BSA_PATTERN_MULTI_DIAGONAL) {
+          const int m = ((d % period) + period) % period;
+          keep = min(m, period - m) <= band;
+        } else if (kind == BSA_PATTERN_STRIPES) {
+          keep = ((stripe_bits[j >> 5] >> (j & 31)) & 1u) || abs(d) <= band;
+        } else {
+          keep = true;                       // BSA_PATTERN_DENSE and unknown kinds
+        }
+        if (keep) word |= 1u << b;
+      }
+      bits[(size_t)r * words + w] = word;
+    }
+    cnt += __popc(word);
+  }
+  cnt = wave_sum_i(cnt);
+  if (lane == 0) counts[r] = cnt;
+}
+
 }  // namespace
 
 EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes) {
@@ -443,6 +540,15 @@ hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const 
                                    int keep_prefix_tokens, const bsa_csr* out, const SelectWs& w, hipStream_t s) {
   const int n_forced = min(p.nb, (keep_prefix_tokens + p.bs - 1) / p.bs);
   launch_select_any<true>(p, mass, top_p, mask, n_forced, w.counts, w.bits, w.words, s);
+  launch_csr(p, w.counts, w.bits, w.words, out, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, const bsa_pattern_params& prm,
+                                  const bsa_csr* out, const SelectWs& w, hipStream_t s) {
+  pattern_kernel<<<(p.R + 3) / 4, kThreads, 0, s>>>(head_kind, p.nb, p.R, p.N, p.bs, prm.prefix_tokens,
+                                                    prm.frame_tokens, prm.band, prm.period, prm.stripes,
+                                                    prm.n_stripes, w.counts, w.bits, w.words);
   launch_csr(p, w.counts, w.bits, w.words, out, s);
   return hipGetLastError();
 }

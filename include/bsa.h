@@ -82,7 +82,8 @@ typedef enum {
   BSA_WS_ESTIMATE = 0,
   BSA_WS_FORWARD = 1,
   BSA_WS_BACKWARD = 2,
-  BSA_WS_SELECT_FROM_MASS = 3
+  BSA_WS_SELECT_FROM_MASS = 3,
+  BSA_WS_STRUCTURED = 4
 } bsa_ws_kind;
 
 /* Bytes of device workspace `kind` needs for `shape` and a CSR of `capacity`
@@ -137,6 +138,51 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
 bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass,
                                 float top_p, int32_t keep_prefix_tokens, bsa_csr* out,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Structured (static) head patterns.  The SVG page (Abstract) sorts heads
+ * into spatial heads, where tokens of the same frame dominate, and temporal
+ * heads, where tokens at the same position in other frames dominate; the
+ * Sparse-vDiT page (Abstract) finds diagonal, multi-diagonal and
+ * vertical-stripe patterns.  Token geometry: tokens [0, prefix_tokens) are
+ * text; video token n >= prefix_tokens is in frame (n - prefix)/frame_tokens
+ * at spatial index (n - prefix) % frame_tokens.
+ *   SPATIAL        a video query token relates to the video keys of its frame;
+ *   TEMPORAL       ... to the video keys at its spatial index, in every frame;
+ *   DIAGONAL       query block i relates to key block j when |i - j| <= band;
+ *   MULTI_DIAGONAL ... when |i - j - k*period| <= band for some integer k;
+ *   STRIPES        ... when j is one of `stripes` or |i - j| <= band;
+ *   DENSE          every pair.
+ * In every pattern pairs with a text token are related, and a block pair is
+ * kept when any of its token pairs is related. */
+typedef enum {
+  BSA_PATTERN_DENSE = 0,
+  BSA_PATTERN_SPATIAL = 1,
+  BSA_PATTERN_TEMPORAL = 2,
+  BSA_PATTERN_DIAGONAL = 3,
+  BSA_PATTERN_MULTI_DIAGONAL = 4,
+  BSA_PATTERN_STRIPES = 5
+} bsa_pattern;
+
+typedef struct {
+  int32_t prefix_tokens;   /* text tokens at the start, in [0, N] */
+  int32_t frame_tokens;    /* video tokens per frame, >= 1 */
+  int32_t band;            /* half-width of the diagonal bands in blocks, >= 0 */
+  int32_t period;          /* spacing of the multi-diagonal bands in blocks, >= 1 */
+  const int32_t* stripes;  /* device array of key-block ids (ids outside [0, nb) ignored), or NULL */
+  int32_t n_stripes;       /* entries of stripes, >= 0 */
+} bsa_pattern_params;
+
+/* Builds the CSR mask of structured head patterns.
+ *   head_kind  [B*H] int32 device array, one bsa_pattern per head (b, h);
+ *              an unknown value gives that head dense rows.
+ *   params     pattern parameters shared by all heads (host struct).
+ *   out        CSR written by the call, rows ascending, exact row_ptr
+ *              offsets and entries past out->capacity dropped, as in
+ *              bsa_estimate_mask (R*nb always suffices).
+ *   ws         at least bsa_workspace_size(shape, BSA_WS_STRUCTURED, 0) bytes.
+ * Only shape->B, H, N and block are used (D and dtype must still be valid). */
+bsa_status bsa_structured_mask(const bsa_shape* shape, const int32_t* head_kind, const bsa_pattern_params* params,
+                               bsa_csr* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Sparse attention forward over a block mask (see the header comment, stage 2).
  *   q, k, v    [B,H,N,D] device tensors of shape->dtype.

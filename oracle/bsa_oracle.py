@@ -299,7 +299,7 @@ def _block_tokens(i: int, block: int, N: int) -> range:
 
 
 def structured_block_mask(kind: int, N: int, block: int, prefix: int, frame_tokens: int, band: int,
-                          period: int, stripes=()) -> np.ndarray:
+                          period: int, stripes=(), rows=None) -> np.ndarray:
     """Block-level mask [nb, nb] of one head for a structured pattern.
 
     Token geometry: tokens [0, prefix) are text; a video token n >= prefix sits
@@ -317,17 +317,19 @@ def structured_block_mask(kind: int, N: int, block: int, prefix: int, frame_toke
     Every pattern also keeps text: pairs with a text query or text key token
     are related.  A block pair (i, j) is kept iff some token pair of it is
     related (for the block patterns, iff the block relation holds or a text
-    token is involved).
+    token is involved).  With ``rows`` only those query blocks are evaluated
+    (the result then has len(rows) rows).
     """
     nb = num_blocks(N, block)
-    rel = np.zeros((nb, nb), dtype=bool)
+    rows = list(range(nb)) if rows is None else [int(i) for i in rows]
+    rel = np.zeros((len(rows), nb), dtype=bool)
     F = max(1, int(frame_tokens))
     stripes = set(int(j) for j in stripes)
     toks = [_block_tokens(i, block, N) for i in range(nb)]
     has_text = [any(n < prefix for n in t) for t in toks]
     frames = [{(n - prefix) // F for n in t if n >= prefix} for t in toks]
     spots = [{(n - prefix) % F for n in t if n >= prefix} for t in toks]
-    for i in range(nb):
+    for ri, i in enumerate(rows):
         for j in range(nb):
             if has_text[i] or has_text[j] or kind == PATTERN_DENSE:
                 ok = True
@@ -343,7 +345,7 @@ def structured_block_mask(kind: int, N: int, block: int, prefix: int, frame_toke
                 ok = j in stripes or abs(i - j) <= band
             else:
                 raise ValueError(f"unknown pattern {kind}")
-            rel[i, j] = ok
+            rel[ri, j] = ok
     return rel
 
 

@@ -27,7 +27,8 @@ def _csr(cap=1024):
 def test_library_exports_every_header_function():
     names = _lib.header_functions()
     assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error",
-                            "bsa_select_from_mass", "bsa_status_string", "bsa_version", "bsa_workspace_size"])
+                            "bsa_select_from_mass", "bsa_status_string", "bsa_structured_mask", "bsa_version",
+                            "bsa_workspace_size"])
     L = _lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -133,6 +134,32 @@ def test_select_from_mass_validation():
     assert call(out=m) == _lib.BSA_ERR_INVALID_ARG                     # mask aliases out
     assert call(ws_bytes=8) == _lib.BSA_ERR_WORKSPACE
     assert call(shape=_shape(block=96)) == _lib.BSA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_structured_mask_validation():
+    L = _lib.load()
+    s = _shape()
+    assert L.bsa_workspace_size(ctypes.byref(s), 4, 0) == L.bsa_workspace_size(ctypes.byref(s), 3, 0)
+
+    def call(kinds=FAKE, prefix=0, frame=16, band=1, period=2, stripes=None, n=0, out=None, ws_bytes=1 << 30,
+             shape=s):
+        prm = _lib.BsaPatternParams(prefix, frame, band, period, stripes, n)
+        o = out if out is not None else _csr()
+        return L.bsa_structured_mask(ctypes.byref(shape), kinds, ctypes.byref(prm), ctypes.byref(o), FAKE,
+                                     ws_bytes, None)
+
+    assert call(kinds=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(prefix=-1) == _lib.BSA_ERR_INVALID_ARG
+    assert call(prefix=1025) == _lib.BSA_ERR_INVALID_ARG
+    assert call(frame=0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(band=-1) == _lib.BSA_ERR_INVALID_ARG
+    assert call(period=0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(n=3) == _lib.BSA_ERR_INVALID_ARG                 # stripes count without an array
+    assert call(n=-1, stripes=FAKE) == _lib.BSA_ERR_INVALID_ARG
+    assert call(ws_bytes=4) == _lib.BSA_ERR_WORKSPACE
+    assert call(out=_lib.BsaCsr(FAKE, None, 5)) == _lib.BSA_ERR_INVALID_ARG
+    assert call(shape=_shape(D=80)) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
