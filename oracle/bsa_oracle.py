@@ -18,6 +18,7 @@ What it computes, in the order the method runs:
 * Mask narrowing: Top-p over the exact block attention weights of an earlier
   step, restricted to that step's blocks (GSRS page, Abstract; Figure 4
   caption) -- the same ranking and cut as the estimator, applied to masses.
+* Token permutation (gather into a space-filling-curve order, scatter back).
 * Structured head masks: the SVG page's spatial and temporal heads and the
   Sparse-vDiT page's diagonal, multi-diagonal and vertical-stripe patterns
   (both Abstracts), lifted from token pairs to block pairs.
@@ -284,6 +285,31 @@ def estimate_mask(Q: np.ndarray, K: np.ndarray, block: int, top_p: float, scale:
         all_rows.extend(r.selected for r in rs)
     row_ptr, col_idx = rows_to_csr(all_rows)
     return row_ptr, col_idx, sels
+
+
+# ----------------------------------------------------------------------------
+# token permutation (layout transformation)
+# ----------------------------------------------------------------------------
+
+def permute_rows(x: np.ndarray, perm: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Reorder the token axis (axis 1 of [heads, N, ...]) by ``perm``.
+
+    Token reordering along a space-filling curve keeps space-time neighbours
+    in the same block (DFSAttn page, Abstract; GSRS page, Figure 1, 3 and 6
+    captions), and the SVG page (Abstract) pairs its kernels with a layout
+    transformation of the tensors.  Gather: y[:, n] = x[:, perm[n]]; inverse
+    (scatter, undoing the gather): y[:, perm[n]] = x[:, n].  An entry of perm
+    outside [0, N) gives a zero row in a gather and is skipped in a scatter.
+    """
+    perm = np.asarray(perm, dtype=np.int64)
+    N = x.shape[1]
+    ok = (perm >= 0) & (perm < N)
+    y = np.zeros_like(x)
+    if not inverse:
+        y[:, ok] = x[:, perm[ok]]
+    else:
+        y[:, perm[ok]] = x[:, ok]
+    return y
 
 
 # ----------------------------------------------------------------------------

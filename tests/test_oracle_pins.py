@@ -262,6 +262,28 @@ def test_narrow_by_mass_on_forward_masses():
 
 
 # ----------------------------------------------------------------------------
+# token permutation
+# ----------------------------------------------------------------------------
+
+def test_permute_rows_by_hand_and_round_trip():
+    x = np.arange(2 * 5 * 3, dtype=np.float64).reshape(2, 5, 3)
+    perm = np.array([3, 0, 4, 1, 2])
+    y = O.permute_rows(x, perm)
+    assert y[0, 0].tolist() == x[0, 3].tolist() and y[1, 2].tolist() == x[1, 4].tolist()
+    assert y[0, :, 0].tolist() == [9.0, 0.0, 12.0, 3.0, 6.0]                 # rows 3, 0, 4, 1, 2 of head 0
+    assert (O.permute_rows(y, perm, inverse=True) == x).all()
+    assert (O.permute_rows(x, np.arange(5)) == x).all()
+    rng = np.random.default_rng(31)
+    p1, p2 = rng.permutation(5), rng.permutation(5)
+    assert (O.permute_rows(O.permute_rows(x, p1), p2) == O.permute_rows(x, p1[p2])).all()
+    bad = np.array([0, 7, 1, -1, 2])
+    z = O.permute_rows(x, bad)
+    assert (z[:, 1] == 0).all() and (z[:, 3] == 0).all() and (z[:, 4] == x[:, 2]).all()
+    w = O.permute_rows(x, bad, inverse=True)
+    assert (w[:, 0] == x[:, 0]).all() and (w[:, 1] == x[:, 2]).all() and (w[:, 3] == 0).all()
+
+
+# ----------------------------------------------------------------------------
 # structured head masks
 # ----------------------------------------------------------------------------
 
