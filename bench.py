@@ -205,6 +205,42 @@ def main(argv=None) -> int:
     sel_ms = s0.elapsed_time(s1) / nsel
     nnz_narrow = int(narrowed.row_ptr[-1].item())
 
+    # Token permutation (space-filling-curve order in for Q, K, V; the inverse
+    # order out for O), timed on its own: an HBM-streaming gather/scatter.
+    from workloads.hilbert import hilbert_order
+    T_, Hg_, Wg_ = w.grid
+    perm_h = np.concatenate([np.arange(w.text_prefix), w.text_prefix + np.asarray(hilbert_order((T_, Hg_, Wg_)))])
+    perm_d = torch.from_numpy(perm_h.astype(np.int32)).to(dev)
+    pq, pk, pv, po = (torch.empty_like(t) for t in (q, k, v, o))
+
+    def permute_all():
+        bsa.bsa_permute_tokens(q, perm_d, out=pq)
+        bsa.bsa_permute_tokens(k, perm_d, out=pk)
+        bsa.bsa_permute_tokens(v, perm_d, out=pv)
+        bsa.bsa_permute_tokens(o, perm_d, inverse=True, out=po)
+
+    permute_all()
+    s0.record(stream)
+    for _ in range(nsel):
+        permute_all()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    perm_ms = s0.elapsed_time(s1) / nsel
+    perm_bytes = 4 * 2.0 * q.numel() * q.element_size()
+    del pq, pk, pv, po
+
+    # Structured head mask (spatial heads over the video frames) generated on the GPU.
+    kinds = torch.full((w.B * w.H,), 1, dtype=torch.int32, device=dev)
+    smask = bsa.bsa_structured_mask(q, kinds, w.block, prefix_tokens=w.text_prefix, frame_tokens=Hg_ * Wg_)
+    s0.record(stream)
+    for _ in range(nsel):
+        bsa.bsa_structured_mask(q, kinds, w.block, prefix_tokens=w.text_prefix, frame_tokens=Hg_ * Wg_, out=smask)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    struct_ms = s0.elapsed_time(s1) / nsel
+    struct_nnz = int(smask.row_ptr[-1].item())
+    del smask
+
     rp, ci = mask.to_host()
     nnz = int(rp[-1])
     pairs = executed_pairs(w.N, w.block, w.B * w.H, rp, ci)
@@ -251,6 +287,11 @@ def main(argv=None) -> int:
     out["select_from_mass"] = {"ms": round(sel_ms, 4), "top_p": p_next, "entries_in": nnz, "entries_out": nnz_narrow,
                                "algorithmic_bytes": sel_bytes,
                                "gbps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1)}
+    out["permute_tokens"] = {"ms": round(perm_ms, 4), "tensors": "gather q, k, v + scatter o",
+                             "bytes": perm_bytes, "gbps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
+                             "pct_hbm_peak": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    out["structured_mask"] = {"ms": round(struct_ms, 4), "pattern": "spatial heads", "nnz": struct_nnz,
+                              "block_density": struct_nnz / (R * w.nb)}
     if w.backward:
         out["bwd_ms"] = round(bwd_ms, 4)
         out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)

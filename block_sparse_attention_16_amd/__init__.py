@@ -5,12 +5,14 @@ sparse FlashAttention-style forward/backward with exact per-block attention
 mass, implemented as hand-written HIP kernels behind a C ABI (libbsa.so,
 declared in include/bsa.h).  This package is a thin torch binding of it.
 """
-from .api import (Csr, bsa_backward, bsa_estimate_mask, bsa_forward, bsa_last_error, bsa_select_from_mass,
+from .api import (Csr, bsa_backward, bsa_estimate_mask, bsa_forward, bsa_last_error, bsa_permute_tokens,
+                  bsa_select_from_mass,
                   bsa_status_string, bsa_structured_mask, bsa_version, bsa_workspace_size, csr_from_host, make_shape,
                   num_rows)
 from ._lib import BsaError, LIB_PATH, load
 
-__all__ = ["Csr", "bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error", "bsa_select_from_mass",
+__all__ = ["Csr", "bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error", "bsa_permute_tokens",
+           "bsa_select_from_mass",
            "bsa_status_string", "bsa_structured_mask",
            "bsa_version", "bsa_workspace_size", "csr_from_host", "make_shape", "num_rows", "BsaError", "LIB_PATH",
            "load"]

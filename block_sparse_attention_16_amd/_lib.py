@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
     L.bsa_select_from_mass.restype = i32
     L.bsa_structured_mask.argtypes = [P(BsaShape), vp, P(BsaPatternParams), P(BsaCsr), vp, sz, vp]
     L.bsa_structured_mask.restype = i32
+    L.bsa_permute_rows.argtypes = [i64, i32, i32, vp, vp, i32, vp, vp]
+    L.bsa_permute_rows.restype = i32
     L.bsa_forward.argtypes = [P(BsaShape), vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
     L.bsa_forward.restype = i32
     L.bsa_backward.argtypes = [P(BsaShape), vp, vp, vp, vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]

@@ -181,6 +181,28 @@ def bsa_structured_mask(q: torch.Tensor, head_kind: torch.Tensor, block: int, pr
     return out
 
 
+def bsa_permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """Token permutation of a [B, H, N, ...] tensor along N (see bsa_permute_rows
+    in include/bsa.h): gather out[:, :, t] = x[:, :, perm[t]], or with
+    ``inverse`` the scatter out[:, :, perm[t]] = x[:, :, t]."""
+    if not x.is_contiguous() or x.dim() < 3:
+        raise ValueError("x must be a contiguous [B, H, N, ...] tensor")
+    n = x.shape[2]
+    if perm.dtype != torch.int32 or perm.numel() != n or perm.device != x.device:
+        raise ValueError("perm must be an int32 tensor of N entries on x's device")
+    perm = perm.contiguous()
+    out = torch.empty_like(x) if out is None else out
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    heads = x.shape[0] * x.shape[1]
+    row_bytes = x.element_size() * (x.numel() // max(1, heads * n))
+    st = load().bsa_permute_rows(int(heads), int(n), int(row_bytes), x.data_ptr(), perm.data_ptr(), int(bool(inverse)),
+                                 out.data_ptr(), _stream())
+    check(st, "bsa_permute_rows")
+    return out
+
+
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Csr, block: int, scale: float = 0.0,
                 want_mass: bool = True, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                 mass: torch.Tensor | None = None, workspace: torch.Tensor | None = None):

@@ -169,6 +169,27 @@ bsa_status bsa_structured_mask(const bsa_shape* shape, const int32_t* head_kind,
                     "structured-mask launch");
 }
 
+bsa_status bsa_permute_rows(int64_t heads, int32_t n, int32_t row_bytes, const void* src, const int32_t* perm,
+                            int32_t inverse, void* dst, void* stream) {
+  g_err[0] = 0;
+  if (heads < 1 || n < 1) return fail(BSA_ERR_INVALID_ARG, "heads=%lld and n=%d must be >= 1", (long long)heads, n);
+  if (row_bytes < 4 || row_bytes % 4 != 0)
+    return fail(BSA_ERR_INVALID_ARG, "row_bytes=%d must be a positive multiple of 4", row_bytes);
+  if (!src || !dst || !perm) return fail(BSA_ERR_INVALID_ARG, "src, dst and perm must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(src) & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u))
+    return fail(BSA_ERR_INVALID_ARG, "src and dst must be 4-byte aligned");
+  if (inverse != 0 && inverse != 1) return fail(BSA_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  const int64_t words = heads * (int64_t)n * (row_bytes / 4);
+  if (heads > (int64_t(1) << 31) / n || words >= (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "heads*n*row_bytes/4 must be below 2^31");
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = (uintptr_t)words * 4;
+  if (a < b + bytes && b < a + bytes) return fail(BSA_ERR_INVALID_ARG, "src and dst overlap");
+  return hip_status(bsa::launch_permute_rows(heads, n, row_bytes, src, perm, inverse == 1, dst,
+                                             static_cast<hipStream_t>(stream)),
+                    "permute launch");
+}
+
 bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v, float scale,
                        const bsa_csr* mask, void* o, float* lse, float* block_mass, void* ws, size_t ws_bytes,
                        void* stream) {

@@ -60,6 +60,10 @@ hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const 
 hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, const bsa_pattern_params& prm,
                                   const bsa_csr* out, const SelectWs& w, hipStream_t s);
 
+// ---- token permutation (permute.hip) ----
+hipError_t launch_permute_rows(int64_t heads, int n, int row_bytes, const void* src, const int32_t* perm,
+                               bool inverse, void* dst, hipStream_t s);
+
 // ---- forward (forward_bf16.hip, forward_fp32.hip) ----
 struct ForwardWs {
   float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)

@@ -184,6 +184,26 @@ typedef struct {
 bsa_status bsa_structured_mask(const bsa_shape* shape, const int32_t* head_kind, const bsa_pattern_params* params,
                                bsa_csr* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Token permutation of [heads, n, row_bytes] slabs.  Reordering tokens along
+ * a space-filling curve keeps space-time neighbours in the same block (DFSAttn
+ * page, Abstract; GSRS page, Figure 1, 3 and 6 captions); the SVG page
+ * (Abstract) pairs its kernels with such a layout transformation.
+ *   heads      number of slabs (e.g. B*H), >= 1.
+ *   n          token rows per slab (e.g. N), >= 1.
+ *   row_bytes  bytes per row, a positive multiple of 4 (D * element size for
+ *              q, k, v, o; 4 for lse).
+ *   perm       [n] int32 device array, normally a permutation of [0, n).
+ *   inverse    0: gather, dst[h, t] = src[h, perm[t]] (into the new order);
+ *              1: scatter, dst[h, perm[t]] = src[h, t] (undoes the gather).
+ *              An entry outside [0, n) gives a zero row in a gather and is
+ *              skipped in a scatter; a perm with repeated entries leaves the
+ *              scatter's result for those rows unspecified.
+ *   src, dst   device arrays of heads*n*row_bytes bytes, 4-byte aligned, not
+ *              overlapping; heads*n*row_bytes/4 must be below 2^31.
+ * 16-byte moves are used when row_bytes and both pointers allow. */
+bsa_status bsa_permute_rows(int64_t heads, int32_t n, int32_t row_bytes, const void* src, const int32_t* perm,
+                            int32_t inverse, void* dst, void* stream);
+
 /* Sparse attention forward over a block mask (see the header comment, stage 2).
  *   q, k, v    [B,H,N,D] device tensors of shape->dtype.
  *   scale      logit scale; <= 0 selects 1/sqrt(D).

@@ -27,7 +27,7 @@ def _csr(cap=1024):
 def test_library_exports_every_header_function():
     names = _lib.header_functions()
     assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error",
-                            "bsa_select_from_mass", "bsa_status_string", "bsa_structured_mask", "bsa_version",
+                            "bsa_permute_rows", "bsa_select_from_mass", "bsa_status_string", "bsa_structured_mask", "bsa_version",
                             "bsa_workspace_size"])
     L = _lib.load()
     for n in names:
@@ -160,6 +160,25 @@ def test_structured_mask_validation():
     assert call(ws_bytes=4) == _lib.BSA_ERR_WORKSPACE
     assert call(out=_lib.BsaCsr(FAKE, None, 5)) == _lib.BSA_ERR_INVALID_ARG
     assert call(shape=_shape(D=80)) == _lib.BSA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_permute_rows_validation():
+    L = _lib.load()
+
+    def call(heads=2, n=16, rb=256, src=FAKE, perm=FAKE + (1 << 20), inv=0, dst=FAKE + (1 << 24)):
+        return L.bsa_permute_rows(heads, n, rb, src, perm, inv, dst, None)
+
+    assert call(heads=0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(n=0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(rb=6) == _lib.BSA_ERR_INVALID_ARG
+    assert call(rb=0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(src=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(perm=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(src=FAKE + 2) == _lib.BSA_ERR_INVALID_ARG           # misaligned
+    assert call(inv=2) == _lib.BSA_ERR_INVALID_ARG
+    assert call(dst=FAKE + 64) == _lib.BSA_ERR_INVALID_ARG           # overlaps src
+    assert call(heads=1 << 20, n=1 << 12, rb=4096) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
