@@ -63,35 +63,54 @@ def load_traffic(kernel: str, workload: str, flop_per_launch: float):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, scale, rp, ci, budget_s: float):
-    """Time the CPU oracle on a seeded sample of mask rows (bounded by budget_s)."""
+def cpu_baseline(x, w, scale, top_p, budget_s: float):
+    """Time the CPU oracle on a bounded, seeded sample of the workload.
+
+    A third of the budget runs the oracle's estimator on whole heads (seeded
+    order); the rest runs the oracle's forward on seeded rows of those heads,
+    over the oracle's own masks.  The rate is the sampled rows' executed FLOP
+    over their forward time plus their share of the estimator time."""
     from oracle import bsa_oracle as O
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    R = w.B * w.H * w.nb
-    order = np.random.default_rng(12345).permutation(R)
-    done, flop, t0 = [], 0.0, time.perf_counter()
-    for r in order:
-        O.sparse_forward(x["q"], x["k"], x["v"], w.block, rp, ci, scale, rows=[int(r)])
-        done.append(int(r))
-        if time.perf_counter() - t0 > budget_s:
+    rng = np.random.default_rng(12345)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    masks, t_est = [], 0.0
+    t0 = time.perf_counter()
+    for hi in rng.permutation(len(heads)):
+        b, h = heads[int(hi)]
+        ts = time.perf_counter()
+        rp_h, ci_h, _ = O.estimate_mask(x["q"], x["k"], w.block, top_p, scale,
+                                        keep_prefix_tokens=w.keep_prefix_tokens, heads=[(b, h)])
+        t_est += time.perf_counter() - ts
+        masks.append((b, h, rp_h, ci_h))
+        if time.perf_counter() - t0 > budget_s / 3:
             break
-    dt = time.perf_counter() - t0
-    sub_rp = np.zeros(len(done) + 1, np.int64)
-    parts = []
-    for n, r in enumerate(done):
-        seg = ci[rp[r]:rp[r + 1]]
-        parts.append(seg)
-        sub_rp[n + 1] = sub_rp[n] + seg.size
+    est_per_row = t_est / (len(masks) * w.nb)
     sizes = np.minimum(w.block, w.N - np.arange(w.nb) * w.block)
-    for n, r in enumerate(done):
-        flop += 4.0 * w.D * sizes[r % w.nb] * sizes[parts[n]].sum()
+    pairs = [(m, i) for m in range(len(masks)) for i in range(w.nb)]
+    flop, t_fwd, n = 0.0, 0.0, 0
+    t1 = time.perf_counter()
+    for pi in rng.permutation(len(pairs)):
+        m, i = pairs[int(pi)]
+        b, h, rp_h, ci_h = masks[m]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ts = time.perf_counter()
+        O.sparse_forward(x["q"][sl], x["k"][sl], x["v"][sl], w.block, rp_h, ci_h, scale, rows=[i])
+        t_fwd += time.perf_counter() - ts
+        flop += 4.0 * w.D * sizes[i] * sizes[ci_h[rp_h[i]:rp_h[i + 1]]].sum()
+        n += 1
+        if time.perf_counter() - t1 > budget_s * 2 / 3:
+            break
+    dt = t_fwd + n * est_per_row
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(done)} of {R} mask rows (seeded random order), float64 numpy oracle on the GPU's "
-                      f"mask, {dt:.1f} s wall", "seconds": dt, "rows": len(done)}
+            "sample": f"float64 numpy oracle: estimator on {len(masks)} of {len(heads)} heads ({t_est:.1f} s), "
+                      f"forward on {n} seeded rows of those heads over the oracle's masks ({t_fwd:.1f} s); "
+                      f"rate = their FLOP / (forward time + their share of the estimator time)",
+            "seconds": t_est + t_fwd, "rows": n}
 
 
 def main(argv=None) -> int:
@@ -296,7 +315,7 @@ def main(argv=None) -> int:
         out["bwd_ms"] = round(bwd_ms, 4)
         out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)
     if not a.no_cpu_baseline:
-        cb = cpu_baseline(x, w, scale, rp, ci, a.cpu_budget)
+        cb = cpu_baseline(x, w, scale, top_p, a.cpu_budget)
         out["cpu_baseline"] = {k2: cb[k2] for k2 in ("value", "unit", "cores", "kind", "sample")}
     else:
         out["cpu_baseline"] = None
