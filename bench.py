@@ -158,6 +158,8 @@ def main(argv=None) -> int:
     if w.backward:
         ws_b = torch.empty(max(bsa.bsa_workspace_size(shape, 2, cap), 256), dtype=torch.uint8, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        # fp32 copy of O from the forward: delta for the backward without a recomputing pass
+        o32 = torch.empty(q.shape, dtype=torch.float32, device=dev)
 
     stream = torch.cuda.current_stream()
     ev = []
@@ -173,11 +175,12 @@ def main(argv=None) -> int:
                               out=mask, workspace=ws_e)
         if record:
             e1.record(stream)
-        bsa.bsa_forward(q, k, v, mask, w.block, out=o, lse=lse, mass=mass, workspace=ws_f)
+        bsa.bsa_forward(q, k, v, mask, w.block, out=o, lse=lse, mass=mass, workspace=ws_f,
+                        o32=o32 if w.backward else None)
         if record:
             e2.record(stream)
         if w.backward:
-            bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block, workspace=ws_b, dq=dq, dk=dk, dv=dv)
+            bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block, workspace=ws_b, dq=dq, dk=dk, dv=dv, o32=o32)
         if record:
             e3.record(stream)
             ev.append((e0, e1, e2, e3))

@@ -64,9 +64,9 @@ def load() -> ctypes.CDLL:
     L.bsa_structured_mask.restype = i32
     L.bsa_permute_rows.argtypes = [i64, i32, i32, vp, vp, i32, vp, vp]
     L.bsa_permute_rows.restype = i32
-    L.bsa_forward.argtypes = [P(BsaShape), vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
+    L.bsa_forward.argtypes = [P(BsaShape), vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, vp, sz, vp]
     L.bsa_forward.restype = i32
-    L.bsa_backward.argtypes = [P(BsaShape), vp, vp, vp, vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
+    L.bsa_backward.argtypes = [P(BsaShape), vp, vp, vp, vp, vp, vp, vp, f32, P(BsaCsr), vp, vp, vp, vp, sz, vp]
     L.bsa_backward.restype = i32
     L.bsa_status_string.argtypes = [i32]
     L.bsa_status_string.restype = ctypes.c_char_p

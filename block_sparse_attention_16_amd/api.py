@@ -205,8 +205,11 @@ def bsa_permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = Fals
 
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Csr, block: int, scale: float = 0.0,
                 want_mass: bool = True, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                mass: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Sparse attention forward -> (O, LSE, block mass or None)."""
+                mass: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                o32: torch.Tensor | None = None):
+    """Sparse attention forward -> (O, LSE, block mass or None).  ``o32``: an
+    optional [B, H, N, D] fp32 tensor that receives O before its rounding to
+    bf16 (bf16 data only), for the single-pass delta of bsa_backward."""
     _check(q, "q")
     _check(k, "k", like=q)
     _check(v, "v", like=q)
@@ -222,18 +225,23 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Csr, bl
         _check(mass, "mass", dtype=torch.float32)
         if mass.numel() < mask.capacity:
             raise ValueError("mass must hold mask.capacity entries")
+    if o32 is not None:
+        _check(o32, "o32", dtype=torch.float32)
+        if o32.shape != q.shape:
+            raise ValueError("o32 must have q's shape")
     ws = _workspace(shape, BSA_WS_FORWARD, mask.capacity, workspace, q.device)
     mc = mask.c()
     st = load().bsa_forward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), float(scale),
-                            ctypes.byref(mc), o.data_ptr(), lse.data_ptr(), _ptr(mass), ws.data_ptr(), ws.numel(),
-                            _stream())
+                            ctypes.byref(mc), o.data_ptr(), lse.data_ptr(), _ptr(mass), _ptr(o32), ws.data_ptr(),
+                            ws.numel(), _stream())
     check(st, "bsa_forward")
     return o, lse, (mass[: mask.capacity] if mass is not None else None)
 
 
 def bsa_backward(q, k, v, o, d_o, lse, mask: Csr, block: int, scale: float = 0.0,
-                 workspace: torch.Tensor | None = None, dq=None, dk=None, dv=None):
-    """Backward of bsa_forward for dL/dO = d_o -> (dQ, dK, dV)."""
+                 workspace: torch.Tensor | None = None, dq=None, dk=None, dv=None, o32=None):
+    """Backward of bsa_forward for dL/dO = d_o -> (dQ, dK, dV).  ``o32``: the
+    forward's fp32 O (bf16 data only) -> delta from it and a single dQ pass."""
     _check(q, "q")
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
         _check(t, n, like=q)
@@ -242,10 +250,14 @@ def bsa_backward(q, k, v, o, d_o, lse, mask: Csr, block: int, scale: float = 0.0
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    if o32 is not None:
+        _check(o32, "o32", dtype=torch.float32)
+        if o32.shape != q.shape:
+            raise ValueError("o32 must have q's shape")
     ws = _workspace(shape, BSA_WS_BACKWARD, mask.capacity, workspace, q.device)
     mc = mask.c()
     st = load().bsa_backward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                             d_o.data_ptr(), lse.data_ptr(), float(scale), ctypes.byref(mc), dq.data_ptr(),
+                             _ptr(o32), d_o.data_ptr(), lse.data_ptr(), float(scale), ctypes.byref(mc), dq.data_ptr(),
                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
     check(st, "bsa_backward")
     return dq, dk, dv

@@ -10,11 +10,13 @@
 //
 // Kernels, in launch order:
 //   delta_kernel  lse2 = LSE * log2(e), padded per head to nb*BS rows (padding
-//                 +inf -> P = 0); on the fp32 path also delta = rowsum(dO * O)
+//                 +inf -> P = 0); with an fp32 O (the fp32 path, or the
+//                 forward's fp32 copy of a bf16 O) also delta = rowsum(dO * O)
 //   csc_kernel    one workgroup per head: counting transpose of the mask, rows
 //                 visited in order so every column lists query blocks ascending
-//   dq_kernel     per query block: S^T = K Q^T, dP^T = V dO^T; pass 1 gives
-//                 delta = sum_k P dP, pass 2 dQ^T += K^T dS^T
+//   dq_kernel     per query block: S^T = K Q^T, dP^T = V dO^T; without a
+//                 given delta, pass 1 computes delta = sum_k P dP; then
+//                 dQ^T += K^T dS^T
 //   dkv_kernel    per key block:   S = Q K^T,   dP = dO V^T,
 //                 dV^T += dO^T P,  dK^T += Q^T dS
 //
@@ -172,8 +174,8 @@ __device__ __forceinline__ void two_products(const char* ta, const char* tb, con
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O), lse2 = LSE * log2(e); [BH, nb*BS] with padding rows.
 // ---------------------------------------------------------------------------
-template <class T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+template <class TO, class TG, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const TO* __restrict__ o, const TG* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ delta,
                                                     float* __restrict__ lse2, int N, int npad, int BH,
                                                     int with_delta) {
@@ -261,9 +263,10 @@ __global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ ro
 // dQ: one workgroup per query block (mask row).  Wave w owns queries
 // [32w, 32w+32); per unit (SUB keys of a visited key block, tiles K, V in LDS):
 //   S^T = K Q^T, P^T = exp2(c2 S^T - lse2_q), dP^T = V dO^T.
-// Pass 1 accumulates delta_q = sum_k P dP over the row in fp32 (equal to
-// dO_q . O_q for the exact O, without the rounding of a bf16 O) and stores it
-// for the dK/dV kernel; pass 2 forms dS^T = P^T (dP^T - delta_q) and
+// Without a given delta (delta_given = 0), pass 1 accumulates
+// delta_q = sum_k P dP over the row in fp32 (equal to dO_q . O_q for the
+// exact O, without the rounding of a bf16 O) and stores it for the dK/dV
+// kernel; the last pass forms dS^T = P^T (dP^T - delta_q) and
 // dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int BS, int D>
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
-    __bf16* __restrict__ dq, int N, int nb, float scale) {
+    __bf16* __restrict__ dq, int N, int nb, float scale, int delta_given) {
   using C = BCfg<BS, D>;
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
@@ -389,11 +392,15 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
   using first_t = std::integral_constant<bool, false>;
   using second_t = std::integral_constant<bool, true>;
   float dsum = 0.f;
-  pass(first_t{}, dsum);
-  my_delta = dsum + __shfl_xor(dsum, 32);
-  if (hf == 0) delta[prow] = my_delta;
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // the last unit's prefetched id
-  __syncthreads();                      // every wave is done with the tiles
+  if (delta_given) {
+    my_delta = delta[prow];
+  } else {
+    pass(first_t{}, dsum);
+    my_delta = dsum + __shfl_xor(dsum, 32);
+    if (hf == 0) delta[prow] = my_delta;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the last unit's prefetched id
+    __syncthreads();                      // every wave is done with the tiles
+  }
   pass(second_t{}, dsum);
 
   if (qq < N) {
@@ -581,17 +588,32 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
 
 template <int BS, int D>
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
-                           float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, const BackwardWs& w,
-                           hipStream_t s) {
+                           float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, bool delta_given,
+                           const BackwardWs& w, hipStream_t s) {
   dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
-      static_cast<__bf16*>(dq), p.N, p.nb, scale);   // also writes delta
+      static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0);   // writes delta when not given
   dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
       static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale);
   return hipGetLastError();
+}
+
+template <class TO, class TG>
+void launch_delta(const Problem& p, const void* o, const void* d_o, const float* lse, int with_delta,
+                  const BackwardWs& w, hipStream_t s) {
+  const int BH = p.B * p.H;
+  const int npad = p.nb * p.bs;
+  const long long rows = (long long)BH * npad;
+  const unsigned grid = (unsigned)((rows * (p.D / 8) + 255) / 256);
+  if (p.D == 64)
+    delta_kernel<TO, TG, 64><<<grid, 256, 0, s>>>(static_cast<const TO*>(o), static_cast<const TG*>(d_o), lse,
+                                                  w.delta, w.lse2, p.N, npad, BH, with_delta);
+  else
+    delta_kernel<TO, TG, 128><<<grid, 256, 0, s>>>(static_cast<const TO*>(o), static_cast<const TG*>(d_o), lse,
+                                                   w.delta, w.lse2, p.N, npad, BH, with_delta);
 }
 
 }  // namespace
@@ -614,35 +636,23 @@ hipError_t launch_backward_fp32(const Problem& p, const void* q, const void* k, 
                                 const BackwardWs& w, hipStream_t s);
 
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,
-                           const void* d_o, const float* lse, float scale, const bsa_csr* mask, void* dq, void* dk,
-                           void* dv, const BackwardWs& w, hipStream_t s) {
-  const int BH = p.B * p.H;
-  const int npad = p.nb * p.bs;
-  const long long rows = (long long)BH * npad;
-  const int lpr = p.D / 8;
-  const unsigned grid_d = (unsigned)((rows * lpr + 255) / 256);
+                           const float* o32, const void* d_o, const float* lse, float scale, const bsa_csr* mask,
+                           void* dq, void* dk, void* dv, const BackwardWs& w, hipStream_t s) {
   const bool bf = p.dtype == BSA_BF16;
-  if (p.D == 64) {
-    if (bf) delta_kernel<__bf16, 64><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
-                                                            static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
-                                                            p.N, npad, BH, 0);
-    else delta_kernel<float, 64><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o), static_cast<const float*>(d_o),
-                                                        lse, w.delta, w.lse2, p.N, npad, BH, 1);
-  } else {
-    if (bf) delta_kernel<__bf16, 128><<<grid_d, 256, 0, s>>>(static_cast<const __bf16*>(o),
-                                                             static_cast<const __bf16*>(d_o), lse, w.delta, w.lse2,
-                                                             p.N, npad, BH, 0);
-    else delta_kernel<float, 128><<<grid_d, 256, 0, s>>>(static_cast<const float*>(o),
-                                                         static_cast<const float*>(d_o), lse, w.delta, w.lse2, p.N,
-                                                         npad, BH, 1);
-  }
-  csc_kernel<<<BH, 256, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start, w.csc_count,
-                                w.csc_row);
+  const bool delta_given = bf && o32 != nullptr;
+  if (!bf) launch_delta<float, float>(p, o, d_o, lse, 1, w, s);
+  else if (delta_given) launch_delta<float, __bf16>(p, o32, d_o, lse, 1, w, s);
+  else launch_delta<__bf16, __bf16>(p, o, d_o, lse, 0, w, s);
+  csc_kernel<<<p.B * p.H, 256, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start,
+                                      w.csc_count, w.csc_row);
   if (!bf) return launch_backward_fp32(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
-  if (p.bs == 128 && p.D == 128) return launch_bwd_bf16<128, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
-  if (p.bs == 128 && p.D == 64) return launch_bwd_bf16<128, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
-  if (p.bs == 64 && p.D == 128) return launch_bwd_bf16<64, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
-  return launch_bwd_bf16<64, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
+  if (p.bs == 128 && p.D == 128)
+    return launch_bwd_bf16<128, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, delta_given, w, s);
+  if (p.bs == 128 && p.D == 64)
+    return launch_bwd_bf16<128, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, delta_given, w, s);
+  if (p.bs == 64 && p.D == 128)
+    return launch_bwd_bf16<64, 128>(p, q, k, v, d_o, scale, mask, dq, dk, dv, delta_given, w, s);
+  return launch_bwd_bf16<64, 64>(p, q, k, v, d_o, scale, mask, dq, dk, dv, delta_given, w, s);
 }
 
 }  // namespace bsa

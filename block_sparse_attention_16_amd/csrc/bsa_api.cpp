@@ -191,8 +191,8 @@ bsa_status bsa_permute_rows(int64_t heads, int32_t n, int32_t row_bytes, const v
 }
 
 bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v, float scale,
-                       const bsa_csr* mask, void* o, float* lse, float* block_mass, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       const bsa_csr* mask, void* o, float* lse, float* block_mass, float* o_f32, void* ws,
+                       size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   bsa::Problem p;
   BSA_TRY(make_problem(shape, &p));
@@ -201,6 +201,10 @@ bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, con
   BSA_TRY(check_tensor(v, "v"));
   BSA_TRY(check_tensor(o, "o"));
   BSA_TRY(check_tensor(lse, "lse"));
+  if (o_f32) {
+    if (p.dtype != BSA_BF16) return fail(BSA_ERR_INVALID_ARG, "o_f32 is for bf16 data only");
+    BSA_TRY(check_tensor(o_f32, "o_f32"));
+  }
   if (!std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is not finite");
   BSA_TRY(check_csr(mask, "mask"));
   size_t need = 0;
@@ -210,14 +214,14 @@ bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, con
   bsa::ForwardWs w = bsa::carve_forward(p, mask->capacity, block_mass != nullptr, ws, &need);
   const float sc = resolve_scale(scale, p.D);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p.dtype == BSA_BF16 ? bsa::launch_forward_bf16(p, q, k, v, sc, mask, o, lse, block_mass, w, s)
+  hipError_t e = p.dtype == BSA_BF16 ? bsa::launch_forward_bf16(p, q, k, v, sc, mask, o, lse, block_mass, o_f32, w, s)
                                      : bsa::launch_forward_fp32(p, q, k, v, sc, mask, o, lse, block_mass, w, s);
   return hip_status(e, "forward launch");
 }
 
 bsa_status bsa_backward(const bsa_shape* shape, const void* q, const void* k, const void* v, const void* o,
-                        const void* d_o, const float* lse, float scale, const bsa_csr* mask, void* dq, void* dk,
-                        void* dv, void* ws, size_t ws_bytes, void* stream) {
+                        const float* o_f32, const void* d_o, const float* lse, float scale, const bsa_csr* mask,
+                        void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   bsa::Problem p;
   BSA_TRY(make_problem(shape, &p));
@@ -230,6 +234,10 @@ bsa_status bsa_backward(const bsa_shape* shape, const void* q, const void* k, co
   BSA_TRY(check_tensor(dq, "dq"));
   BSA_TRY(check_tensor(dk, "dk"));
   BSA_TRY(check_tensor(dv, "dv"));
+  if (o_f32) {
+    if (p.dtype != BSA_BF16) return fail(BSA_ERR_INVALID_ARG, "o_f32 is for bf16 data only");
+    BSA_TRY(check_tensor(o_f32, "o_f32"));
+  }
   if (!std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is not finite");
   BSA_TRY(check_csr(mask, "mask"));
   size_t need = 0;
@@ -237,7 +245,7 @@ bsa_status bsa_backward(const bsa_shape* shape, const void* q, const void* k, co
   if (ws_bytes < need || (need && !ws))
     return fail(BSA_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", need, ws_bytes);
   bsa::BackwardWs w = bsa::carve_backward(p, mask->capacity, ws, &need);
-  return hip_status(bsa::launch_backward(p, q, k, v, o, d_o, lse, resolve_scale(scale, p.D), mask, dq, dk, dv, w,
+  return hip_status(bsa::launch_backward(p, q, k, v, o, o_f32, d_o, lse, resolve_scale(scale, p.D), mask, dq, dk, dv, w,
                                          static_cast<hipStream_t>(stream)),
                     "backward launch");
 }

@@ -70,7 +70,7 @@ struct ForwardWs {
 };
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes);
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
-                               const bsa_csr* mask, void* o, float* lse, float* mass,
+                               const bsa_csr* mask, void* o, float* lse, float* mass, float* o32,
                                const ForwardWs& w, hipStream_t s);
 hipError_t launch_forward_fp32(const Problem& p, const void* q, const void* k, const void* v, float scale,
                                const bsa_csr* mask, void* o, float* lse, float* mass,
@@ -86,7 +86,7 @@ struct BackwardWs {
 };
 BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes);
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,
-                           const void* d_o, const float* lse, float scale, const bsa_csr* mask,
+                           const float* o32, const void* d_o, const float* lse, float scale, const bsa_csr* mask,
                            void* dq, void* dk, void* dv, const BackwardWs& w, hipStream_t s);
 
 }  // namespace bsa

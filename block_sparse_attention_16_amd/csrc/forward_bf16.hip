@@ -284,7 +284,8 @@ template <int BS, int D>
 __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two waves per SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, int N, int nb, float scale) {
+    float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, float* __restrict__ o32, int N,
+    int nb, float scale) {
   using C = Cfg<BS, D>;
   // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
   // the compiler see that reads of one tile do not wait on the DMA into another.
@@ -465,6 +466,16 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * hf) = out4;
       }
     }
+    if (o32 != nullptr) {              // O before its rounding to bf16
+      float* frow = o32 + ((size_t)bh * N + qq) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(frow + dt * 32 + 8 * g + 4 * hf) =
+              make_float4(acc[dt][g * 4] * inv, acc[dt][g * 4 + 1] * inv, acc[dt][g * 4 + 2] * inv,
+                          acc[dt][g * 4 + 3] * inv);
+    }
   }
   if (mass == nullptr || n_e == 0) return;
   __syncthreads();
@@ -484,23 +495,25 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 
 template <int BS, int D>
 hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const void* v, float scale,
-                       const bsa_csr* mask, void* o, float* lse, float* mass, const ForwardWs& w, hipStream_t s) {
+                       const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
+                       hipStream_t s) {
   using C = Cfg<BS, D>;
   fwd_kernel<BS, D><<<p.R, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
-      mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, p.N, p.nb, scale);
+      mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
+      scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
-                               const bsa_csr* mask, void* o, float* lse, float* mass, const ForwardWs& w,
+                               const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
                                hipStream_t s) {
-  if (p.bs == 128 && p.D == 128) return launch_bs_d<128, 128>(p, q, k, v, scale, mask, o, lse, mass, w, s);
-  if (p.bs == 128 && p.D == 64) return launch_bs_d<128, 64>(p, q, k, v, scale, mask, o, lse, mass, w, s);
-  if (p.bs == 64 && p.D == 128) return launch_bs_d<64, 128>(p, q, k, v, scale, mask, o, lse, mass, w, s);
-  return launch_bs_d<64, 64>(p, q, k, v, scale, mask, o, lse, mass, w, s);
+  if (p.bs == 128 && p.D == 128) return launch_bs_d<128, 128>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
+  if (p.bs == 128 && p.D == 64) return launch_bs_d<128, 64>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
+  if (p.bs == 64 && p.D == 128) return launch_bs_d<64, 128>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
+  return launch_bs_d<64, 64>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
 }
 
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes) {

@@ -216,18 +216,27 @@ bsa_status bsa_permute_rows(int64_t heads, int32_t n, int32_t row_bytes, const v
  *              for entry (i, j), the mean over the valid queries of block i of
  *              the softmax probability that falls on key block j (each row
  *              sums to 1).
+ *   o_f32      NULL, or (BSA_BF16 only) a [B,H,N,D] fp32 output receiving O
+ *              before its rounding to bf16, for bsa_backward's single-pass
+ *              delta.  Must be NULL for BSA_FP32 (o is already fp32).
  *   ws         at least bsa_workspace_size(shape, BSA_WS_FORWARD, capacity) bytes. */
 bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, const void* v,
                        float scale, const bsa_csr* mask, void* o, float* lse,
-                       float* block_mass, void* ws, size_t ws_bytes, void* stream);
+                       float* block_mass, float* o_f32, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the sparse forward for a loss L with dL/dO = d_o.
  *   o, lse     the forward's outputs for the same q, k, v, scale and mask.
+ *   o_f32      NULL, or (BSA_BF16 only) the forward's o_f32 output: then
+ *              delta_q = dO_q . O_q is taken from it and dQ needs one pass
+ *              over the row.  With NULL (or for BSA_FP32 data) delta is
+ *              computed exactly as sum_k P dP in a first pass, because the
+ *              rounding of a bf16 O moves it by more than the gradients can
+ *              absorb.
  *   dq, dk, dv [B,H,N,D] outputs of shape->dtype (overwritten, not accumulated).
  *   ws         at least bsa_workspace_size(shape, BSA_WS_BACKWARD, capacity) bytes.
  * Deterministic: no floating-point atomics. */
 bsa_status bsa_backward(const bsa_shape* shape, const void* q, const void* k, const void* v,
-                        const void* o, const void* d_o, const float* lse, float scale,
+                        const void* o, const float* o_f32, const void* d_o, const float* lse, float scale,
                         const bsa_csr* mask, void* dq, void* dk, void* dv,
                         void* ws, size_t ws_bytes, void* stream);
 

@@ -99,18 +99,27 @@ def test_forward_and_backward_validation():
     s = _shape()
     m = _csr()
     args = [FAKE] * 3
-    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 16, None)
+    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, ctypes.byref(m), FAKE, FAKE, FAKE, None, FAKE, 16, None)
     assert st == _lib.BSA_ERR_WORKSPACE
-    st = L.bsa_forward(ctypes.byref(s), FAKE, None, FAKE, 0.0, ctypes.byref(m), FAKE, FAKE, None, FAKE, 1 << 30,
+    st = L.bsa_forward(ctypes.byref(s), FAKE, None, FAKE, 0.0, ctypes.byref(m), FAKE, FAKE, None, None, FAKE,
+                       1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, None, FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, ctypes.byref(m), FAKE, FAKE, None, FAKE + 4, FAKE, 1 << 30,
                        None)
-    assert st == _lib.BSA_ERR_INVALID_ARG
-    st = L.bsa_forward(ctypes.byref(s), *args, 0.0, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
-    assert st == _lib.BSA_ERR_INVALID_ARG
-    st = L.bsa_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0.0, ctypes.byref(m), FAKE, FAKE,
-                        FAKE, FAKE, 1 << 30, None)
-    assert st == _lib.BSA_ERR_INVALID_ARG
-    st = L.bsa_backward(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, ctypes.byref(m), FAKE,
+    assert st == _lib.BSA_ERR_INVALID_ARG                               # misaligned o_f32
+    st = L.bsa_forward(ctypes.byref(_shape(dtype=1)), *args, 0.0, ctypes.byref(m), FAKE, FAKE, None, FAKE, FAKE,
+                       1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG                               # o_f32 with fp32 data
+    st = L.bsa_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 0.0, ctypes.byref(m), FAKE,
                         FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG
+    st = L.bsa_backward(ctypes.byref(_shape(dtype=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0,
+                        ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.BSA_ERR_INVALID_ARG                               # o_f32 with fp32 data
+    st = L.bsa_backward(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.0, ctypes.byref(m),
+                        FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == _lib.BSA_ERR_UNSUPPORTED
 
 

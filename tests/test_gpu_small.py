@@ -216,10 +216,10 @@ def test_host_validation_errors(bsa):
     assert e.value.status == 2
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dtype,delta", [("bf16", "exact"), ("bf16", "o32"), ("fp32", "exact")])
 @pytest.mark.parametrize("D,bs", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("N", [37, 300])
-def test_backward_random_masks_ragged(bsa, dtype, D, bs, N):
+def test_backward_random_masks_ragged(bsa, dtype, delta, D, bs, N):
     from tests.gpu_helpers import compare_backward
     rng = np.random.default_rng(7 * N + D + bs)
     B, H = 1, 2
@@ -237,10 +237,16 @@ def test_backward_random_masks_ragged(bsa, dtype, D, bs, N):
     rp, ci = O.rows_to_csr(rows)
     mask = bsa.csr_from_host(rp, ci, "cuda")
     qd, kd, vd, gd = (to_device(t, dtype) for t in (q, k, v, g))
-    o, lse, _ = bsa.bsa_forward(qd, kd, vd, mask, bs, want_mass=False)
-    dq, dk, dv = bsa.bsa_backward(qd, kd, vd, o, gd, lse, mask, bs)
+    o32 = torch.empty(qd.shape, dtype=torch.float32, device="cuda") if delta == "o32" else None
+    o, lse, _ = bsa.bsa_forward(qd, kd, vd, mask, bs, want_mass=False, o32=o32)
+    dq, dk, dv = bsa.bsa_backward(qd, kd, vd, o, gd, lse, mask, bs, o32=o32)
     torch.cuda.synchronize()
     x = {"q": q, "k": k, "v": v, "g": g}
+    if o32 is not None:
+        # the fp32 copy of O agrees with the oracle without the bf16 store rounding
+        o_ref, _, _ = O.sparse_forward(q, k, v, bs, rp, ci, default_scale(D))
+        assert np.abs(to_host(o32) - o_ref).max() < TOL["bf16"]["o"]
+        assert np.abs(to_host(o32) - to_host(o)).max() <= 2.0 ** -8 * np.abs(to_host(o32)).max() + 1e-30
     err = compare_backward(x, bs, rp, ci, default_scale(D), [(0, 0), (0, 1)],
                            {"dq": to_host(dq), "dk": to_host(dk), "dv": to_host(dv)}, dtype)
     assert err["excess"] <= 0.0, f"gradient errors {err}"

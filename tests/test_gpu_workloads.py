@@ -75,17 +75,19 @@ def test_wan_reduced_search_steps(bsa):
                 assert set(ci[rp[r]:rp[r + 1]].tolist()) <= set(fci[frp[r]:frp[r + 1]].tolist())
 
 
-def test_dsv_training_forward_and_backward(bsa):
+@pytest.mark.parametrize("delta", ["exact", "o32"])
+def test_dsv_training_forward_and_backward(bsa, delta):
     from tests.gpu_helpers import compare_backward
     w = get("dsv_train")
     x = make_inputs(w, dtype="bf16", want_grad=True)
     mask, (rp, ci) = _run_step(bsa, w, x, f32(w.top_p[0]))
     q, k, v, g = (to_device(x[n], "bf16") for n in "qkvg")
-    o, lse, _ = bsa.bsa_forward(q, k, v, mask, w.block, want_mass=False)
-    dq, dk, dv = bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block)
+    o32 = torch.empty(q.shape, dtype=torch.float32, device="cuda") if delta == "o32" else None
+    o, lse, _ = bsa.bsa_forward(q, k, v, mask, w.block, want_mass=False, o32=o32)
+    dq, dk, dv = bsa.bsa_backward(q, k, v, o, g, lse, mask, w.block, o32=o32)
     torch.cuda.synchronize()
     heads = [(0, 0), (1, w.H - 1)]
     grads = {"dq": to_host(dq), "dk": to_host(dk), "dv": to_host(dv)}
     err = compare_backward(x, w.block, rp, ci, default_scale(w.D), heads, grads, "bf16")
-    print(f"[{w.name}] gradient errors on heads {heads}: {err}", flush=True)
+    print(f"[{w.name} delta={delta}] gradient errors on heads {heads}: {err}", flush=True)
     assert err["excess"] <= 0.0, f"gradient errors {err}"
