@@ -280,7 +280,9 @@ __device__ __forceinline__ void phase_c(const char* vs, const bf16x8 (&pb)[C::KC
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BS, int D>
+// WRITE_O32: also store O in fp32 (a separate instantiation, so that the
+// common kernel is compiled without the extra epilogue).
+template <int BS, int D, bool WRITE_O32>
 __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two waves per SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * hf) = out4;
       }
     }
-    if (o32 != nullptr) {              // O before its rounding to bf16
+    if constexpr (WRITE_O32) {         // O before its rounding to bf16
       float* frow = o32 + ((size_t)bh * N + qq) * D;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -498,10 +500,16 @@ hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const voi
                        const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
                        hipStream_t s) {
   using C = Cfg<BS, D>;
-  fwd_kernel<BS, D><<<p.R, C::THREADS, 0, s>>>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
-      mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
-      scale);
+  if (o32 != nullptr)
+    fwd_kernel<BS, D, true><<<p.R, C::THREADS, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
+        mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
+        scale);
+  else
+    fwd_kernel<BS, D, false><<<p.R, C::THREADS, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
+        mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, nullptr, p.N,
+        p.nb, scale);
   return hipGetLastError();
 }
 
