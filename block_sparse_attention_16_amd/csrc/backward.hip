@@ -274,14 +274,16 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
-    __bf16* __restrict__ dq, int N, int nb, float scale, int delta_given) {
+    __bf16* __restrict__ dq, int N, int nb, float scale, int delta_given, const int32_t* __restrict__ order,
+    int t0) {
   using C = BCfg<BS, D>;
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
 
-  const int r = blockIdx.x;
+  // head-major rows up to t0, the grid's last rows longest first (order)
+  const int r = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
   const int bh = r / nb, i = r - bh * nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
     const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ csc_start, const int32_t* __restrict__ csc_count,
     const int32_t* __restrict__ csc_row, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, int nb,
-    float scale) {
+    float scale, const int32_t* __restrict__ order, int t0) {
   using C = BCfg<BS, D>;
   __shared__ __attribute__((aligned(1024))) char q0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char q1s[C::TILE_BYTES];
@@ -439,7 +441,8 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
   __shared__ __attribute__((aligned(16))) float ld0s[2 * C::SUB];   // lse2 rows, then delta rows
   __shared__ __attribute__((aligned(16))) float ld1s[2 * C::SUB];
 
-  const int c = blockIdx.x;                      // column = bh * nb + j
+  // column = bh * nb + j: head-major up to t0, the last columns longest first
+  const int c = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
   const int bh = c / nb, j = c - bh * nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -590,14 +593,18 @@ template <int BS, int D>
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
                            float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, bool delta_given,
                            const BackwardWs& w, hipStream_t s) {
+  const int T = tail_rows(p.R), t0 = p.R - T;
+  launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, T, w.order_q, s);
+  launch_tail_order(nullptr, 0, w.csc_count, t0, T, w.order_k, s);
   dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
-      static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0);   // writes delta when not given
+      static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0,   // writes delta when not given
+      w.order_q, t0);
   dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
-      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale);
+      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale, w.order_k, t0);
   return hipGetLastError();
 }
 
@@ -627,6 +634,10 @@ BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* 
   w.csc_start = c.take<int32_t>((size_t)p.R);
   w.csc_count = c.take<int32_t>((size_t)p.R);
   w.csc_row = c.take<int32_t>((size_t)(capacity > 0 ? capacity : 1));
+  if (p.dtype == BSA_BF16) {
+    w.order_q = c.take<int32_t>(tail_rows(p.R));
+    w.order_k = c.take<int32_t>(tail_rows(p.R));
+  }
   *bytes = align_up(c.off, 256);
   return w;
 }

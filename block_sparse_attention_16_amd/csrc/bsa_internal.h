@@ -64,9 +64,22 @@ hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, co
 hipError_t launch_permute_rows(int64_t heads, int n, int row_bytes, const void* src, const int32_t* perm,
                                bool inverse, void* dst, hipStream_t s);
 
+// ---- longest-first order of a grid's last rows (order.hip) ----
+// Rows [R - T, R), T = tail_rows(R), run longest first; order[t] is the row
+// that workgroup R - T + t takes.  2048 rows measured best of 1024/2048/4096
+// on the four video workloads (four rounds of the 512 resident 128-token
+// forward workgroups).
+constexpr int kTailRows = 2048;
+inline int tail_rows(int R) { return R < kTailRows ? R : kTailRows; }
+// Lengths are counts[r] when counts is non-null, else the CSR extents of
+// row_ptr clamped to [0, cap].
+void launch_tail_order(const int32_t* row_ptr, int64_t cap, const int32_t* counts, int r0, int T, int32_t* order,
+                       hipStream_t s);
+
 // ---- forward (forward_bf16.hip, forward_fp32.hip) ----
 struct ForwardWs {
   float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)
+  int32_t* order;    // [tail_rows(R)] rows of the grid's tail, longest first
 };
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes);
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
@@ -83,6 +96,8 @@ struct BackwardWs {
   int32_t* csc_start;  // [B*H*nb] first transposed entry of key-block column (bh, j)
   int32_t* csc_count;  // [B*H*nb] query blocks in that column
   int32_t* csc_row;    // [capacity] query block of each transposed entry
+  int32_t* order_q;    // [tail_rows(R)] dQ grid's last rows, longest first
+  int32_t* order_k;    // [tail_rows(R)] dK/dV grid's last columns, longest first
 };
 BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes);
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,

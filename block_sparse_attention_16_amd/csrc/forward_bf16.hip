@@ -287,7 +287,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, float* __restrict__ o32, int N,
-    int nb, float scale) {
+    int nb, float scale, const int32_t* __restrict__ order, int t0) {
   using C = Cfg<BS, D>;
   // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
   // the compiler see that reads of one tile do not wait on the DMA into another.
@@ -300,7 +300,9 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   // blockIdx -> mask row, dealt to the 8 XCDs round-robin by the dispatcher
   // (finer-grained than any contiguous split, which balances rows of unequal
   // length; keeping neighbouring rows on one XCD's L2 measured no faster).
-  const int r = blockIdx.x;
+  // Head-major up to t0, so that rows running together share K/V in the
+  // caches; the last rows of the grid longest first (order).
+  const int r = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
   const int bh = r / nb, i = r - bh * nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
@@ -500,16 +502,18 @@ hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const voi
                        const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
                        hipStream_t s) {
   using C = Cfg<BS, D>;
+  const int T = tail_rows(p.R), t0 = p.R - T;
+  launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, T, w.order, s);
   if (o32 != nullptr)
     fwd_kernel<BS, D, true><<<p.R, C::THREADS, 0, s>>>(
         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
         mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
-        scale);
+        scale, w.order, t0);
   else
     fwd_kernel<BS, D, false><<<p.R, C::THREADS, 0, s>>>(
         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
         mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, nullptr, p.N,
-        p.nb, scale);
+        p.nb, scale, w.order, t0);
   return hipGetLastError();
 }
 
@@ -528,6 +532,7 @@ ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void
   Carver c(ws);
   ForwardWs w{};
   if (want_mass) w.part = c.take<float>((size_t)capacity * p.bs);
+  if (p.dtype == BSA_BF16) w.order = c.take<int32_t>(tail_rows(p.R));
   *bytes = align_up(c.off, 256);
   return w;
 }
