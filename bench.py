@@ -113,6 +113,54 @@ def cpu_baseline(x, w, scale, top_p, budget_s: float):
             "seconds": t_est + t_fwd, "rows": n}
 
 
+def density_sweep(torch, bsa, steps: int, warmup: int) -> int:
+    """Forward latency against block density on seeded random masks (the
+    density sweep of the GSRS page's Figure 5 shape; context, not the metric)."""
+    B, H, N, D, bs = 1, 24, 115200, 128, 128
+    nb = -(-N // bs)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    q, k, v = (torch.randn((B, H, N, D), generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+    rng = np.random.default_rng(0)
+    R = B * H * nb
+    for dens in (0.05, 0.1, 0.2, 0.3, 0.5, 1.0):
+        rows = []
+        for r in range(R):
+            i = r % nb
+            kk = max(1, int(round(dens * nb)))
+            if kk >= nb:
+                sel = np.arange(nb)
+            else:
+                others = rng.choice(np.delete(np.arange(nb), i), size=kk - 1, replace=False)
+                sel = np.sort(np.concatenate([[i], others]))           # the diagonal block is always kept
+            rows.append(sel)
+        counts = np.array([len(x) for x in rows])
+        rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        ci = np.concatenate(rows).astype(np.int32)
+        mask = bsa.csr_from_host(rp, ci, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(bsa.bsa_workspace_size(bsa.make_shape(B, H, N, D, bs, 0), 1, ci.size), dtype=torch.uint8,
+                         device=dev)
+        for _ in range(max(1, warmup)):
+            bsa.bsa_forward(q, k, v, mask, bs, want_mass=False, out=o, lse=lse, workspace=ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            bsa.bsa_forward(q, k, v, mask, bs, want_mass=False, out=o, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flop = 4.0 * D * executed_pairs(N, bs, B * H, rp.astype(np.int64), ci.astype(np.int64))
+        print(json.dumps({"sweep": "block density", "density": dens, "nnz": int(ci.size), "fwd_ms": round(ms, 4),
+                          "executed_tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                          "pct_bf16_peak": round(100 * flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                          "shape": {"B": B, "H": H, "N": N, "D": D, "block": bs}}), flush=True)
+        del mask, ws
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +169,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="cogvideox")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--density-sweep", action="store_true",
+                    help="instead of the step: forward latency and TFLOP/s over seeded random block masks of "
+                         "density 5-100%% at B=1, H=24, N=115200, D=128, block 128 (one JSON line per density)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run one plain device-to-device copy of BYTES bytes "
                          "(reference point for HBM byte counters under rocprofv3 --pmc)")
@@ -133,6 +184,9 @@ def main(argv=None) -> int:
     import torch
     import block_sparse_attention_16_amd as bsa
     from workloads import get, make_inputs, bf16_bits
+
+    if a.density_sweep:
+        return density_sweep(torch, bsa, a.steps, a.warmup)
 
     w = get(a.workload)
     dev = torch.device("cuda:0")
@@ -227,6 +281,25 @@ def main(argv=None) -> int:
     sel_ms = s0.elapsed_time(s1) / nsel
     nnz_narrow = int(narrowed.row_ptr[-1].item())
 
+    # Reduced search (multi-step workloads): later steps score only the blocks
+    # step 1 kept; timed on its own at step 2's threshold.
+    red = None
+    if w.reduced_search and len(w.top_p) > 1:
+        p2 = float(np.float32(w.top_p[1]))
+        cand_out = bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev),
+                           torch.empty(cap, dtype=torch.int32, device=dev))
+        bsa.bsa_estimate_mask(q, k, p2, w.block, candidate=mask, keep_prefix_tokens=w.keep_prefix_tokens,
+                              out=cand_out, workspace=ws_e)
+        s0.record(stream)
+        for _ in range(nsel):
+            bsa.bsa_estimate_mask(q, k, p2, w.block, candidate=mask, keep_prefix_tokens=w.keep_prefix_tokens,
+                                  out=cand_out, workspace=ws_e)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        red = {"ms": round(s0.elapsed_time(s1) / nsel, 4), "top_p": p2,
+               "entries_out": int(cand_out.row_ptr[-1].item())}
+        del cand_out
+
     # Token permutation (space-filling-curve order in for Q, K, V; the inverse
     # order out for O), timed on its own: an HBM-streaming gather/scatter.
     from workloads.hilbert import hilbert_order
@@ -309,6 +382,10 @@ def main(argv=None) -> int:
     out["select_from_mass"] = {"ms": round(sel_ms, 4), "top_p": p_next, "entries_in": nnz, "entries_out": nnz_narrow,
                                "algorithmic_bytes": sel_bytes,
                                "gbps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1)}
+    if red is not None:
+        red_bytes = 2.0 * w.B * w.H * w.N * w.D * 2 + 8.0 * (R + 1) + 4.0 * nnz + 4.0 * red["entries_out"]
+        red["gbps"] = round(red_bytes / (red["ms"] * 1e-3) / 1e9, 1)
+        out["estimator_reduced_search"] = red
     out["permute_tokens"] = {"ms": round(perm_ms, 4), "tensors": "gather q, k, v + scatter o",
                              "bytes": perm_bytes, "gbps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
                              "pct_hbm_peak": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
