@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSortMax = 4096;   // largest candidate row (nb <= 4096)
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <class T>
 struct Load8;
@@ -151,15 +152,143 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
   }
 }
 
+// Wave-wide reductions as a butterfly of VALU lane exchanges: DPP quad
+// permutes (lane ^ 1, lane ^ 2), DPP row mirrors (within 8, within 16 lanes),
+// then v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (halves).
+// Each step combines a lane's value with its partner's; partners hold the
+// same two operands, so with a commutative op every lane ends with the
+// bitwise-same result (no LDS traffic, unlike ds_bpermute shuffles).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  x = op(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dpp<0x141>(x));   // row_half_mirror
+  x = op(x, dpp<0x140>(x));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  return __uint_as_float(wave_reduce(__float_as_uint(x), [](uint32_t u, uint32_t v) {
+    return __float_as_uint(__uint_as_float(u) + __uint_as_float(v));
+  }));
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
+  return (int)wave_reduce((uint32_t)x, [](uint32_t u, uint32_t v) { return u + v; });
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  return wave_reduce(x, [](uint32_t u, uint32_t v) { return u > v ? u : v; });
+}
+__device__ __forceinline__ float wave_fmax(float x) {
+  return __uint_as_float(wave_reduce(__float_as_uint(x), [](uint32_t u, uint32_t v) {
+    return __float_as_uint(fmaxf(__uint_as_float(u), __uint_as_float(v)));
+  }));
+}
+// Uniform copy of a value that every lane already holds.
+__device__ __forceinline__ float uniform(float x) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
+}
+
+// Full search (no candidate rows), one mask row per wavefront, 4 per
+// workgroup: lane l holds blocks j = 64e + l, e < EPL.  Same Top-p rule as
+// select_kernel below (bisection for the cut logit L*, blocks above it kept,
+// blocks at L* added in ascending id until the mass reaches p * Z), with
+// every per-block decision in registers: the selection of element e is one
+// ballot, whose two halves are bitmask words 2e and 2e + 1.
+template <int EPL>
+__global__ __launch_bounds__(kThreads) void select_full_kernel(const float* __restrict__ logits, int nb, int R,
+                                                               float top_p, int n_forced,
+                                                               int32_t* __restrict__ counts,
+                                                               uint32_t* __restrict__ bits, int words) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;                        // whole wavefront leaves together
+  const float* lrow = logits + (size_t)r * nb;
+  uint32_t key[EPL];                         // ordered logit bits; 0 = no block
+  float ev[EPL];
+  uint32_t kmax = 0u;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  for (int e = 0; e < EPL; ++e) {
+    const int t = e * 64 + lane;
+    const bool ok = t < nb;
+    const float sv = lrow[ok ? t : 0];
+    key[e] = ok ? ordered_bits(sv) : 0u;
+    ev[e] = sv;
+    kmax = max(kmax, key[e]);
+  }
+  kmax = wave_umax(kmax);
+  const float smax = unordered_bits(kmax);
+  float zl = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    ev[e] = key[e] ? __builtin_amdgcn_exp2f((ev[e] - smax) * kLog2e) : 0.f;
+    zl += ev[e];
+  }
+  const float Z = uniform(wave_sum(zl));
+  uint32_t cut = 1u;                         // keep every block by default
+  int k_tie = -1;                            // >= 0: tied blocks at the cut to add
+  if (top_p < 1.0f && Z > 0.f) {
+    const float thr = top_p * Z;
+    uint32_t T = 0u;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m += key[e] >= c ? ev[e] : 0.f;
+      if (uniform(wave_sum(m)) >= thr) T = c;
+    }
+    cut = T;                                 // L*: M(L*) >= p Z > M(L* + 1)
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) nt += key[e] == T ? 1 : 0;
+    const int n_tie = __builtin_amdgcn_readfirstlane(wave_sum_i(nt));
+    if (n_tie > 1) {
+      float mg = 0.f, et = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        mg += key[e] > T ? ev[e] : 0.f;
+        if (key[e] == T) et = ev[e];
+      }
+      const float m_gt = uniform(wave_sum(mg));
+      const float etie = uniform(wave_fmax(et));   // tied blocks share one weight
+      // add tied blocks one at a time, as a walk in ascending id would
+      float acc = m_gt;
+      k_tie = 0;
+      while (k_tie < n_tie) {
+        acc += etie;
+        ++k_tie;
+        if (acc >= thr) break;
+      }
+    }
+  }
+  const int forced = min(n_forced, nb);
+  int cnt = 0, tied_before = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const bool present = key[e] != 0u;
+    bool take = present && (k_tie >= 0 ? key[e] > cut : key[e] >= cut);
+    if (k_tie >= 0) {
+      const bool tied = present && key[e] == cut;
+      const uint64_t tb = __ballot(tied);
+      const int rank = tied_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0u));
+      take = take || (tied && rank < k_tie);
+      tied_before += __popcll(tb);
+    }
+    uint64_t sel = __ballot(take);
+    const int nf = forced - e * 64;          // forced blocks j < n_forced in this element
+    if (nf > 0) sel |= nf >= 64 ? ~0ull : ((1ull << nf) - 1ull);
+    cnt += __popcll(sel);
+    const int w = 2 * e + (lane & 1);
+    if (lane < 2 && w < words) bits[(size_t)r * words + w] = (uint32_t)(sel >> (32 * (lane & 1)));
+  }
+  if (lane == 0) counts[r] = cnt;
 }
 
 // One mask row per wavefront (4 rows per workgroup).  Lane l holds candidate
@@ -231,8 +360,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  kmax = wave_umax(kmax);
   const float smax = kmax ? unordered_bits(kmax) : 0.f;
   float ev[EPL];
   float zl = 0.f;
@@ -269,8 +397,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       float etie = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) if (key[e] == T) etie = ev[e];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) etie = fmaxf(etie, __shfl_xor(etie, off));
+      etie = wave_fmax(etie);
       // mark the tied ids, then one lane walks them in ascending order
       for (int w = lane; w < words; w += 64) my_seen[w] = 0u;
       __builtin_amdgcn_wave_barrier();
@@ -521,7 +648,21 @@ hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float
     if (bf) launch_pool_logits<__bf16, 128>(p, q, k, scale, w, s);
     else launch_pool_logits<float, 128>(p, q, k, scale, w, s);
   }
-  launch_select_any<false>(p, w.logits, top_p, cand, n_forced, w.counts, w.bits, w.words, s);
+  if (cand) {
+    launch_select_any<false>(p, w.logits, top_p, cand, n_forced, w.counts, w.bits, w.words, s);
+  } else {
+    const unsigned g = (unsigned)((p.R + 3) / 4);
+    if (p.nb <= 64)
+      select_full_kernel<1><<<g, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, n_forced, w.counts, w.bits, w.words);
+    else if (p.nb <= 256)
+      select_full_kernel<4><<<g, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, n_forced, w.counts, w.bits, w.words);
+    else if (p.nb <= 1024)
+      select_full_kernel<16><<<g, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, n_forced, w.counts, w.bits,
+                                                   w.words);
+    else
+      select_full_kernel<64><<<g, kThreads, 0, s>>>(w.logits, p.nb, p.R, top_p, n_forced, w.counts, w.bits,
+                                                   w.words);
+  }
   launch_csr(p, w.counts, w.bits, w.words, out, s);
   return hipGetLastError();
 }
