@@ -8,8 +8,8 @@
 //
 // Kernels, in launch order:
 //   pool_kernel     HBM-streaming mean of Q and K over every token block
-//   logits_kernel   pooled logits scale * Qbar Kbar^T per head, a register-
-//                   tiled fp32 GEMM (each Kbar row is reused by 64 query rows)
+//   logits_kernel   pooled logits scale * Qbar Kbar^T per head, an fp32 GEMM
+//                   on the matrix cores in 64 x 64 tiles
 //   select_kernel   one wavefront per row: softmax over the row's candidates,
 //                   Top-p cut found by bisection on the ordered logit bits
 //                   (no sort), ties at the cut broken by lower block id,
@@ -106,49 +106,44 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
 }
 
 // Pooled logits L[bh, i, j] = scale * <Qbar_i, Kbar_j> for one 64 x 64 tile
-// of one head; 256 threads, each a 4 x 4 block of outputs, d summed in order.
-// grid (ceil(nb/64), ceil(nb/64), B*H).
+// of one head on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32
+// products, fp32 accumulation, twice the rate of the vector FMA path).  256
+// threads; wave w computes the 32 x 32 sub-tile (w / 2, w % 2), d summed in
+// ascending pairs.  grid (ceil(nb/64), ceil(nb/64), B*H).
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 template <int D>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar,
                                                           float* __restrict__ logits, int nb, float scale) {
-  constexpr int DC = 32;                  // d chunk staged in LDS
+  constexpr int DC = 32;                  // d chunk staged in LDS, transposed to [d][row]
   __shared__ __attribute__((aligned(16))) float qs[DC][68];
   __shared__ __attribute__((aligned(16))) float ks[DC][68];
   const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const int l32 = lane & 31, hi = lane >> 5;
   const float* qh = qbar + (size_t)bh * nb * D;
   const float* kh = kbar + (size_t)bh * nb * D;
-  float acc[4][4] = {};
+  floatx16 acc = {};
   for (int d0 = 0; d0 < D; d0 += DC) {
-    // stage 64 rows x 32 dims of Qbar and Kbar, transposed to [d][row]
     for (int x = tid; x < 64 * DC; x += kThreads) {
       const int row = x / DC, d = x % DC;
       qs[d][row] = i0 + row < nb ? qh[(size_t)(i0 + row) * D + d0 + d] : 0.f;
       ks[d][row] = j0 + row < nb ? kh[(size_t)(j0 + row) * D + d0 + d] : 0.f;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < DC; ++d) {
-      const float4 a = *reinterpret_cast<const float4*>(&qs[d][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&ks[d][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    // A[m][k] = Qbar[wi + m][d0 + kk + k] from lane m + 32k; B[k][n] = Kbar[wj + n][d0 + kk + k]
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(av[u], bv[w], acc[u][w]);
-    }
+    for (int kk = 0; kk < DC; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[kk + hi][wi + l32], ks[kk + hi][wj + l32], acc, 0, 0, 0);
     __syncthreads();
   }
+  // accumulator element v of lane l: row 8(v/4) + 4(l/32) + v%4, column l%32
+  const int j = j0 + wj + l32;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty * 4 + u;
-    if (i >= nb) continue;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx * 4 + w;
-      if (j < nb) logits[((size_t)bh * nb + i) * nb + j] = acc[u][w] * scale;
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int i = i0 + wi + 8 * (v >> 2) + 4 * hi + (v & 3);
+    if (i < nb && j < nb) logits[((size_t)bh * nb + i) * nb + j] = acc[v] * scale;
   }
 }
 
@@ -439,33 +434,58 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   if (lane == 0) counts[r] = cnt;
 }
 
-// Exclusive scan of counts[R] into row_ptr[R+1]; a single workgroup of 1024 threads.
+// Exclusive scan of counts[R] into row_ptr[R+1]: one workgroup of 1024
+// threads; per pass of 8192 rows each thread scans 8 consecutive counts in
+// registers, and one wave-and-workgroup scan of the thread totals gives the
+// offsets.  counts is workspace memory (16-byte aligned); row_ptr is the
+// caller's and is stored by dwords.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr,
                                                     int R) {
   __shared__ int wtot[16];
-  __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < R; base += 1024) {
-    const int idx = base + tid;
-    const int v = idx < R ? counts[idx] : 0;
-    int x = v;
+  int carry = 0;
+  for (int base = 0; base < R; base += 8192) {
+    const int i0 = base + tid * 8;
+    int v[8];
+    if (i0 + 8 <= R) {
+      const int4 a = *reinterpret_cast<const int4*>(counts + i0);
+      const int4 b = *reinterpret_cast<const int4*>(counts + i0 + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = i0 + k < R ? counts[i0 + k] : 0;
+    }
+    int sum = 0;                      // v becomes the exclusive scan within the thread
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = v[k];
+      v[k] = sum;
+      sum += c;
+    }
+    int x = sum;                      // inclusive scan of the thread totals over the wave
+#pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off);
+      const int y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
     if (lane == 63) wtot[wid] = x;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wid; ++w) wbase += wtot[w];
-    const int carry = carry_s;
-    if (idx < R) row_ptr[idx] = carry + wbase + x - v;
-    __syncthreads();
-    if (tid == 1023) carry_s = carry + wbase + x;
-    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int t = wtot[w];
+      wbase += w < wid ? t : 0;
+      total += t;
+    }
+    const int off = carry + wbase + x - sum;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (i0 + k < R) row_ptr[i0 + k] = off + v[k];
+    carry += total;
+    __syncthreads();                  // wtot is rewritten by the next pass
   }
-  if (tid == 0) row_ptr[R] = carry_s;
+  if (tid == 0) row_ptr[R] = carry;
 }
 
 // One wavefront per row: set bits -> ascending block ids at row_ptr[r].
