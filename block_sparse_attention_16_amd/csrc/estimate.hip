@@ -64,26 +64,42 @@ struct Load8<float> {
 // Mean over the valid tokens of one block, for Q and K at once.
 // grid.x = R (one workgroup per (b, h, block)); 256 threads.
 // Thread t reads the 8-element chunk (t % (D/8)) of rows t/(D/8), +G, ...
-template <class T, int D>
+// A full block (the common case) issues all of a thread's loads before
+// summing any, so that 16-32 of them are in flight per thread.
+template <class T, int D, int BS>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                         float* __restrict__ qbar, float* __restrict__ kbar,
-                                                        int N, int bs, int nb) {
+                                                        int N, int nb) {
   constexpr int CPR = D / 8;            // chunks per row
   constexpr int G = kThreads / CPR;     // row groups
+  constexpr int ITER = BS / G;          // rows per thread in a full block
   __shared__ float part[2][G][D];
   const int r = blockIdx.x;             // = bh * nb + i
   const int bh = r / nb, i = r - bh * nb;
-  const int lo = i * bs;
-  const int nv = min(bs, N - lo);
+  const int lo = i * BS;
+  const int nv = min(BS, N - lo);
   const int c = threadIdx.x % CPR, g = threadIdx.x / CPR;
   float sq[8] = {}, sk[8] = {};
   const size_t base = ((size_t)bh * N + lo) * D + c * 8;
-  for (int t = g; t < nv; t += G) {
-    float a[8], b[8];
-    Load8<T>::get(q + base + (size_t)t * D, a);
-    Load8<T>::get(k + base + (size_t)t * D, b);
+  if (nv == BS) {
+    float a[ITER][8], b[ITER][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { sq[e] += a[e]; sk[e] += b[e]; }
+    for (int it = 0; it < ITER; ++it) {
+      Load8<T>::get(q + base + (size_t)(g + it * G) * D, a[it]);
+      Load8<T>::get(k + base + (size_t)(g + it * G) * D, b[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sq[e] += a[it][e]; sk[e] += b[it][e]; }
+  } else {
+    for (int t = g; t < nv; t += G) {
+      float a[8], b[8];
+      Load8<T>::get(q + base + (size_t)t * D, a);
+      Load8<T>::get(k + base + (size_t)t * D, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sq[e] += a[e]; sk[e] += b[e]; }
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) { part[0][g][c * 8 + e] = sq[e]; part[1][g][c * 8 + e] = sk[e]; }
@@ -627,8 +643,12 @@ EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes) {
 template <class T, int D>
 static void launch_pool_logits(const Problem& p, const void* q, const void* k, float scale, const EstimateWs& w,
                                hipStream_t s) {
-  pool_kernel<T, D><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar, w.kbar,
-                                             p.N, p.bs, p.nb);
+  if (p.bs == 128)
+    pool_kernel<T, D, 128><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
+                                                    w.kbar, p.N, p.nb);
+  else
+    pool_kernel<T, D, 64><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
+                                                   w.kbar, p.N, p.nb);
   const dim3 g((p.nb + 63) / 64, (p.nb + 63) / 64, p.B * p.H);
   logits_kernel<D><<<g, kThreads, 0, s>>>(w.qbar, w.kbar, w.logits, p.nb, scale);
 }
