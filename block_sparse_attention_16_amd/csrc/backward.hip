@@ -421,25 +421,90 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per key block (bh, j).  Wave w owns keys
-// [32w, 32w+32); per unit (SUB queries of a query block of column j: tiles
-// Q, dO and their lse2 / delta rows in LDS):
+// [32w, 32w+32); the column's query blocks stream through LDS as 32-query
+// tiles (Q, dO and their lse2 / delta rows).  Per tile:
 //   S = Q K^T, P = exp2(c2 S - lse2_q), dP = dO V^T, dS = P (dP - delta_q),
 //   dV^T += dO^T P, dK^T += Q^T dS.
+// Software pipeline one tile deep: iteration t computes S and dP of tile
+// t + 1 with the P / dS arithmetic of tile t interleaved under those MFMAs,
+// then the dV / dK MFMAs of tile t.  Tiles t and t + 1 are read while tile
+// t + 2 is copied in, so three LDS slots rotate (three distinct objects at
+// fixed places of a 3x-unrolled loop).  At D = 128 the K, V fragments and
+// both accumulators fill the register file for one wave per SIMD, with no
+// other wave to hide the VALU work; the pipeline puts it under the MFMAs.
 // ---------------------------------------------------------------------------
 template <int BS, int D>
-__global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D = 128 needs the whole register file
+struct KvCfg {
+  static constexpr int NW = BS / 32;                  // waves, 32 keys each
+  static constexpr int THREADS = NW * 64;
+  static constexpr int TPB = BS / 32;                 // 32-query tiles per query block
+  static constexpr int DS = D / 16, DT = D / 32, CPR = D / 8;
+  static constexpr int TILE_BYTES = 32 * D * 2;       // one Q or dO tile
+  static constexpr int LOADS = TILE_BYTES / (16 * THREADS);
+  static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
+  static_assert(LOADS >= 1 && LOADS * 16 * THREADS == TILE_BYTES, "tile must split evenly over the waves");
+  static_assert(3 * (2 * TILE_BYTES + 256) * (4 * WAVES_PER_SIMD / NW) <= 160 * 1024, "LDS of the resident groups");
+};
+
+template <class C>
+__device__ __forceinline__ uint32_t kv_src_off(int it, int wave, int lane) {
+  const int L = (it * C::NW + wave) * 64 + lane;
+  const int row = L / C::CPR, pos = L % C::CPR;
+  return (uint32_t)((row * (C::CPR * 8) + (pos ^ swz<C::CPR>(row)) * 8) * 2);
+}
+
+// Phase A of a dK/dV iteration: S and dP of the next tile (A operands read
+// row-wise from tiles ta / tb, K^T / V^T fragments in registers), with the
+// current tile's s -> P and dp -> dS interleaved, NE / DS elements per k-step.
+template <int D>
+__device__ __forceinline__ void kv_phase_a(const char* ta, const char* tb, const bf16x8 (&kf)[D / 16],
+                                           const bf16x8 (&vf)[D / 16], floatx16& sn, floatx16& dpn, floatx16& s,
+                                           floatx16& dp, const float (&lv)[16], const float (&dv)[16], bool valid,
+                                           float c2, int l32, int hf) {
+  constexpr int DS = D / 16, CPR = D / 8, AHEAD = 2, EPS = 16 / DS;
+  const floatx16 zero = {};
+  bf16x8 fa[DS], fb[DS];
+#pragma unroll
+  for (int ds = 0; ds < AHEAD; ++ds) {
+    fa[ds] = read_row8<CPR>(ta, l32, ds * 2 + hf);
+    fb[ds] = read_row8<CPR>(tb, l32, ds * 2 + hf);
+  }
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (ds + AHEAD < DS) {
+      fa[ds + AHEAD] = read_row8<CPR>(ta, l32, (ds + AHEAD) * 2 + hf);
+      fb[ds + AHEAD] = read_row8<CPR>(tb, l32, (ds + AHEAD) * 2 + hf);
+    }
+    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ds], kf[ds], ds == 0 ? zero : sn, 0, 0, 0);
+    dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ds], vf[ds], ds == 0 ? zero : dpn, 0, 0, 0);
+#pragma unroll
+    for (int x = ds * EPS; x < (ds + 1) * EPS; ++x) {
+      const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[x], c2, -lv[x])) : 0.f;
+      s[x] = p;
+      dp[x] = p * (dp[x] - dv[x]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BS, int D>
+__global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // KvCfg::WAVES_PER_SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ csc_start, const int32_t* __restrict__ csc_count,
     const int32_t* __restrict__ csc_row, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, int nb,
     float scale, const int32_t* __restrict__ order, int t0) {
-  using C = BCfg<BS, D>;
-  __shared__ __attribute__((aligned(1024))) char q0s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char q1s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char g0s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char g1s[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float ld0s[2 * C::SUB];   // lse2 rows, then delta rows
-  __shared__ __attribute__((aligned(16))) float ld1s[2 * C::SUB];
+  using C = KvCfg<BS, D>;
+  __shared__ __attribute__((aligned(1024))) char qa[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qc[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ga[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char gb[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char gc[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float la[64];   // lse2 of the tile's 32 rows, then their delta
+  __shared__ __attribute__((aligned(16))) float lb[64];
+  __shared__ __attribute__((aligned(16))) float lc[64];
 
   // column = bh * nb + j: head-major up to t0, the last columns longest first
   const int c = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
@@ -451,7 +516,7 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
   const int kk = j * BS + kloc;
   const int start = csc_start[c];
   const int n_e = csc_count[c];
-  const int n_u = n_e * C::U;
+  const int n_t = n_e * C::TPB;                     // 32-query tiles of the column
   const auto qh = raw_rsrc(q + (size_t)bh * N * D, N * D * 2);
   const auto gh = raw_rsrc(dout + (size_t)bh * N * D, N * D * 2);
   const auto lr = raw_rsrc(lse2 + (size_t)bh * nb * BS, nb * BS * 4);
@@ -472,7 +537,7 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
 
   uint32_t off[C::LOADS];
 #pragma unroll
-  for (int it = 0; it < C::LOADS; ++it) off[it] = dma_src_off<BS, D>(it, wave, lane);
+  for (int it = 0; it < C::LOADS; ++it) off[it] = kv_src_off<C>(it, wave, lane);
 
   floatx16 adk[C::DT], adv[C::DT];
 #pragma unroll
@@ -480,95 +545,102 @@ __global__ __launch_bounds__(2 * BS, D == 128 ? 1 : 2) void dkv_kernel(   // D =
 #pragma unroll
     for (int e = 0; e < 16; ++e) { adk[dt][e] = 0.f; adv[dt][e] = 0.f; }
 
-  // first padded query row of unit u (-1: invalid entry)
-  auto unit_row = [&](int ib, int u) { return (ib >= 0 && ib < nb) ? ib * BS + (u % C::U) * C::SUB : -1; };
-  auto row_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(rowr, (u / C::U) * 4, 0, 0); };
-  // tiles of unit rows [row0, row0 + SUB): Q, dO, and (wave 0) the lse2 and delta rows
-  auto dma_unit = [&](int row0, char* qs, char* gs, float* ls) __attribute__((always_inline)) {
-    const int r0 = row0 < 0 ? 0 : row0;
-    dma_tiles<BS, D>(qh, gh, r0, qs, gs, wave, off);
+  // first padded query row of tile t of entry id ib (-1: invalid entry)
+  auto tile_row = [&](int ib, int t) { return (ib >= 0 && ib < nb) ? ib * BS + (t % C::TPB) * 32 : -1; };
+  auto id_load = [&](int t) { return __builtin_amdgcn_raw_buffer_load_b32(rowr, (t / C::TPB) * 4, 0, 0); };
+  // Q and dO rows [row0, row0 + 32) and (wave 0) their lse2 and delta
+  auto dma = [&](int row0, char* qs, char* gs, float* ls) __attribute__((always_inline)) {
+    const uint32_t r0 = (uint32_t)(row0 < 0 ? 0 : row0);
+    const uint32_t base = r0 * (D * 2);
+#pragma unroll
+    for (int it = 0; it < C::LOADS; ++it) {
+      lds_dma16(qh, base + off[it], qs + (it * C::NW + wave) * 64 * 16);
+      lds_dma16(gh, base + off[it], gs + (it * C::NW + wave) * 64 * 16);
+    }
     if (wave == 0) {
-      if constexpr (C::SUB == 32) {
-        // lanes 0-31: lse2 rows, lanes 32-63: delta rows
-        const uint32_t o = (uint32_t)(r0 + l32) * 4;
-        if (hf == 0) lds_dma4(lr, o, ls);
-        else lds_dma4(dr, o, ls);
-      } else {
-        lds_dma4(lr, (uint32_t)(r0 + lane) * 4, ls);
-        lds_dma4(dr, (uint32_t)(r0 + lane) * 4, ls + C::SUB);
-      }
+      // lanes 0-31: lse2 rows, lanes 32-63: delta rows
+      const uint32_t o = (r0 + l32) * 4;
+      if (hf == 0) lds_dma4(lr, o, ls);
+      else lds_dma4(dr, o, ls);
     }
   };
 
-  int iv0 = 0, iv1 = 0;
-  if (n_u > 0) {
-    iv0 = csc_row[start];
-    dma_unit(unit_row(iv0, 0), q0s, g0s, ld0s);
-    iv1 = row_load(1);
-  }
-
-  auto unit = [&](int u, const char* qs, const char* gs, const float* ls, char* qn, char* gn, float* ln)
-                  __attribute__((always_inline)) {
+  floatx16 s, dp;                  // S and dP of the current tile
+  int id0 = 0, id1 = 0, id2 = 0;   // entry ids of tiles t, t + 1, t + 2
+  if (n_t > 0) {
+    id0 = csc_row[start];
+    dma(tile_row(id0, 0), qa, ga, la);
+    if (n_t > 1) {
+      id1 = csc_row[start + 1 / C::TPB];
+      dma(tile_row(id1, 1), qb, gb, lb);
+    }
+    id2 = id_load(2);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    const bool valid = unit_row(__builtin_amdgcn_readfirstlane(iv0), u) >= 0 && kvalid;
-    const int row1 = unit_row(__builtin_amdgcn_readfirstlane(iv1), u + 1);
-    if (u + 1 < n_u) dma_unit(row1, qn, gn, ln);
-    iv0 = iv1;
-    iv1 = row_load(u + 2);
-    // S and dP, one 32-query tile at a time: lane holds key column kloc and
-    // query rows {8a + 4h + r}
+    two_products<D>(qa, ga, kf, vf, s, dp, 0, l32, hf);
+  }
+
+  // Iteration t: tile t in slot (qs, gs, ls), tile t + 1 in (qn, gn), tile
+  // t + 2 copied into (qd, gd, ld), the slot of tile t - 1.  For the last
+  // tile the next tile's S and dP come from a stale slot and are discarded.
+  auto iter = [&](int t, const char* qs, const char* gs, const float* ls, const char* qn, const char* gn, char* qd,
+                  char* gd, float* ld) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile t + 1 and id2 landed
+    __syncthreads();                      // every wave is past tile t - 1
+    const bool valid = tile_row(__builtin_amdgcn_readfirstlane(id0), t) >= 0 && kvalid;
+    if (t + 2 < n_t) dma(tile_row(__builtin_amdgcn_readfirstlane(id2), t + 2), qd, gd, ld);
+    const int id3 = id_load(t + 3);
+    float lv[16], dvv[16];
 #pragma unroll
-    for (int qt = 0; qt < C::KC; ++qt) {
-      floatx16 s, dp;
-      two_products<D>(qs, gs, kf, vf, s, dp, qt * 32, l32, hf);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = qt * 32 + 8 * g + 4 * hf;       // 4 consecutive query rows of the unit
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + qr);
-        const float4 d4 = *reinterpret_cast<const float4*>(ls + C::SUB + qr);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int x = g * 4 + r4;
-          const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[x], c2, -lv[r4])) : 0.f;
-          s[x] = p;
-          dp[x] = p * (dp[x] - dv4[r4]);
-        }
-      }
-      const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 1);
-      const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 1);
-      // step st: d tile st % DT, 16-query half (st / DT) & 1, dV (st < 2 DT) or
-      // dK; consecutive MFMAs update different accumulators
-      constexpr int NS = 4 * C::DT, AHEAD = 2;
-      auto rd = [&](int st) {
-        const char* t = st >= 2 * C::DT ? qs : gs;
-        return read_tr8<C::CPR>(t, qt * 32 + 16 * ((st / C::DT) & 1), (st % C::DT) * 32, lane);
-      };
-      bf16x8 a[NS];
-#pragma unroll
-      for (int st = 0; st < AHEAD; ++st) a[st] = rd(st);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + AHEAD < NS) a[st + AHEAD] = rd(st + AHEAD);
-        const int dt = st % C::DT, half = (st / C::DT) & 1;
-        if (st >= 2 * C::DT)
-          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? d1 : d0, adk[dt], 0, 0, 0);
-        else
-          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? p1 : p0, adv[dt], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 4; ++g) {
+      const int qr = 8 * g + 4 * hf;      // 4 consecutive query rows of the tile
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + qr);
+      const float4 d4 = *reinterpret_cast<const float4*>(ls + 32 + qr);
+      lv[4 * g] = l4.x; lv[4 * g + 1] = l4.y; lv[4 * g + 2] = l4.z; lv[4 * g + 3] = l4.w;
+      dvv[4 * g] = d4.x; dvv[4 * g + 1] = d4.y; dvv[4 * g + 2] = d4.z; dvv[4 * g + 3] = d4.w;
     }
+    floatx16 sn, dpn;
+    kv_phase_a<D>(qn, gn, kf, vf, sn, dpn, s, dp, lv, dvv, valid, c2, l32, hf);
+    const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 1);
+    const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 1);
+    // dV, dK: step st = d tile st % DT, 16-query half (st / DT) & 1, dV for
+    // st < 2 DT, then dK; consecutive MFMAs update different accumulators
+    constexpr int NS = 4 * C::DT, AHEAD = 2;
+    auto rd = [&](int st) {
+      const char* tt = st >= 2 * C::DT ? qs : gs;
+      return read_tr8<C::CPR>(tt, 16 * ((st / C::DT) & 1), (st % C::DT) * 32, lane);
+    };
+    bf16x8 a[NS];
+#pragma unroll
+    for (int st = 0; st < AHEAD; ++st) a[st] = rd(st);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + AHEAD < NS) a[st + AHEAD] = rd(st + AHEAD);
+      const int dt = st % C::DT, half = (st / C::DT) & 1;
+      if (st >= 2 * C::DT)
+        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? d1 : d0, adk[dt], 0, 0, 0);
+      else
+        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st], half ? p1 : p0, adv[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s = sn;
+    dp = dpn;
+    id0 = id1;
+    id1 = id2;
+    id2 = id3;
   };
 
-  int u = 0;
-  for (; u + 1 < n_u; u += 2) {
-    unit(u, q0s, g0s, ld0s, q1s, g1s, ld1s);
-    unit(u + 1, q1s, g1s, ld1s, q0s, g0s, ld0s);
+  int t = 0;
+  for (; t + 2 < n_t; t += 3) {
+    iter(t, qa, ga, la, qb, gb, qc, gc, lc);
+    iter(t + 1, qb, gb, lb, qc, gc, qa, ga, la);
+    iter(t + 2, qc, gc, lc, qa, ga, qb, gb, lb);
   }
-  if (u < n_u) unit(u, q0s, g0s, ld0s, q1s, g1s, ld1s);
+  if (t < n_t) {
+    iter(t, qa, ga, la, qb, gb, qc, gc, lc);
+    if (t + 1 < n_t) iter(t + 1, qb, gb, lb, qc, gc, qa, ga, la);
+  }
 
   if (kk < N) {
     __bf16* krow = dk + ((size_t)bh * N + kk) * D;
