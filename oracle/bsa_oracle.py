@@ -15,6 +15,10 @@ What it computes, in the order the method runs:
   (logit descending, block index ascending) and keep the shortest prefix
   whose cumulative probability reaches p; blocks that hold prefix (text)
   tokens are added afterwards.
+* Hierarchical block scoring (DFSAttn page, Abstract; named there without a
+  definition -- the reading is stated at ``hierarchical_logits``): block
+  logits as the log-sum-exp of the query block mean against the key block's
+  sub-block means, then the same softmax, Top-p and forced blocks.
 * Mask narrowing: Top-p over the exact block attention weights of an earlier
   step, restricted to that step's blocks (GSRS page, Abstract; Figure 4
   caption) -- the same ranking and cut as the estimator, applied to masses.
@@ -65,6 +69,39 @@ def pool_blocks(x: np.ndarray, block: int) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     spans = block_spans(x.shape[0], block)
     return np.stack([x[lo:hi].mean(axis=0) for lo, hi in spans])
+
+
+def sub_block_spans(n_tokens: int, block: int, sub_blocks: int) -> list[list[tuple[int, int]]]:
+    """Token ranges of the sub-blocks of every block: block j splits into
+    ``sub_blocks`` parts of block // sub_blocks tokens; parts that start past
+    the last token are dropped, so a partial last block keeps its non-empty
+    parts (the last of them possibly partial)."""
+    w = block // sub_blocks
+    return [[(a, min(a + w, hi)) for a in range(lo, lo + block, w) if a < hi]
+            for lo, hi in block_spans(n_tokens, block)]
+
+
+def hierarchical_logits(q: np.ndarray, k: np.ndarray, block: int, sub_blocks: int, scale: float) -> np.ndarray:
+    """Block logits of hierarchical block scoring for one (b, h): [nb, nb].
+
+    Reading of the DFSAttn page's hierarchical block scoring (Abstract; the
+    page gives no definition): each query block's mean is scored against the
+    means of the key block's sub-blocks, scale * <Qbar_i, Kbar_{j,m}>, and the
+    key block's logit is the natural log-sum-exp over its non-empty sub-blocks.
+    A block's softmax probability is then the sum of its sub-blocks'
+    probabilities under a softmax over all sub-blocks, so one strongly matched
+    sub-block is not averaged away.  sub_blocks = 1 is the mean-pool logit.
+    """
+    qbar = pool_blocks(q, block)
+    k = np.asarray(k, dtype=np.float64)
+    spans = sub_block_spans(k.shape[0], block, sub_blocks)
+    out = np.empty((qbar.shape[0], len(spans)))
+    for j, parts in enumerate(spans):
+        ksub = np.stack([k[a:b].mean(axis=0) for a, b in parts])     # [parts, D]
+        s = float(scale) * (qbar @ ksub.T)                            # [nb, parts]
+        mx = s.max(axis=1)
+        out[:, j] = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    return out
 
 
 def forced_blocks(keep_prefix_tokens: int, block: int, nb: int) -> np.ndarray:
@@ -235,12 +272,16 @@ def mass_band(row: RowSelection, top_p: float, mass_tol: float = 1e-5) -> set[in
 
 def estimate_head(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale: float,
                   candidate_rows: list[np.ndarray] | None = None,
-                  keep_prefix_tokens: int = 0) -> list[RowSelection]:
-    """Estimator for one (b, h): q, k [N, D] -> one RowSelection per query block."""
-    qbar = pool_blocks(q, block)
-    kbar = pool_blocks(k, block)
-    nb = qbar.shape[0]
-    logits = float(scale) * (qbar @ kbar.T)      # [nb, nb] pooled scores
+                  keep_prefix_tokens: int = 0, sub_blocks: int = 1) -> list[RowSelection]:
+    """Estimator for one (b, h): q, k [N, D] -> one RowSelection per query block.
+    sub_blocks > 1 scores with ``hierarchical_logits``."""
+    if sub_blocks == 1:
+        qbar = pool_blocks(q, block)
+        kbar = pool_blocks(k, block)
+        logits = float(scale) * (qbar @ kbar.T)      # [nb, nb] pooled scores
+    else:
+        logits = hierarchical_logits(q, k, block, sub_blocks, scale)
+    nb = logits.shape[0]
     forced = forced_blocks(keep_prefix_tokens, block, nb)
     rows = []
     for i in range(nb):
@@ -265,7 +306,8 @@ def rows_to_csr(rows: list[np.ndarray]) -> tuple[np.ndarray, np.ndarray]:
 
 def estimate_mask(Q: np.ndarray, K: np.ndarray, block: int, top_p: float, scale: float,
                   candidate: tuple[np.ndarray, np.ndarray] | None = None,
-                  keep_prefix_tokens: int = 0, heads: list[tuple[int, int]] | None = None):
+                  keep_prefix_tokens: int = 0, heads: list[tuple[int, int]] | None = None,
+                  sub_blocks: int = 1):
     """Estimator over [B, H, N, D]; rows ordered (b, h, i).
 
     Returns (row_ptr, col_idx, selections) where selections maps (b, h) to the
@@ -280,7 +322,7 @@ def estimate_mask(Q: np.ndarray, K: np.ndarray, block: int, top_p: float, scale:
     for b, h in pairs:
         base = (b * H + h) * nb
         cr = cand_rows[base:base + nb] if cand_rows is not None else None
-        rs = estimate_head(Q[b, h], K[b, h], block, top_p, scale, cr, keep_prefix_tokens)
+        rs = estimate_head(Q[b, h], K[b, h], block, top_p, scale, cr, keep_prefix_tokens, sub_blocks)
         sels[(b, h)] = rs
         all_rows.extend(r.selected for r in rs)
     row_ptr, col_idx = rows_to_csr(all_rows)

@@ -545,3 +545,68 @@ def test_backward_dv_closed_form_and_zero_row_sums():
     # the shift changes the logits by scale*q.shift per query row, which the
     # softmax removes, so P (and dS) are unchanged and dQ moves by scale*dS@shift = 0
     assert np.abs(dQ2 - dQ).max() < 1e-10
+
+
+# ----------------------------------------------------------------------------
+# hierarchical block scoring (reading of the DFSAttn page, Abstract)
+# ----------------------------------------------------------------------------
+
+def test_hierarchical_hand_worked_fixture():
+    rows, q, k = [], None, None
+    with open(os.path.join(GOLDEN, "hier_stripe_hand_worked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, rest = [x.strip() for x in line.split("|", 1)]
+            if head in ("q", "k"):
+                arr = np.array([[float(v) for v in t.split(",")] for t in rest.split()])
+                if head == "q":
+                    q = arr
+                else:
+                    k = arr
+                continue
+            p, sel = [x.strip() for x in rest.split("|")]
+            rows.append((int(head), float(p), sorted(int(v) for v in sel.split())))
+    assert q.shape == (12, 2) and k.shape == (12, 2) and len(rows) == 7
+    for g, p, want in rows:
+        for r in O.estimate_head(q, k, 4, p, 1.0, sub_blocks=g):
+            assert sorted(r.selected.tolist()) == want, (g, p)
+
+
+def test_hierarchical_g1_is_mean_pool_logit():
+    rng = np.random.default_rng(11)
+    q, k = rng.standard_normal((37, 8)), rng.standard_normal((37, 8))
+    want = 0.3 * (O.pool_blocks(q, 8) @ O.pool_blocks(k, 8).T)
+    np.testing.assert_allclose(O.hierarchical_logits(q, k, 8, 1, 0.3), want, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("g", [2, 4, 8])
+def test_hierarchical_block_probability_is_sum_of_sub_block_probabilities(g):
+    # pure-Python loops over tokens: sub-block means (ragged tail), a softmax
+    # over every sub-block of the row, summed per key block
+    rng = np.random.default_rng(20 + g)
+    N, D, bs, scale = 37, 3, 16, 0.7
+    q, k = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    nb = -(-N // bs)
+    w = bs // g
+    qbar, parts = [], []
+    for i in range(nb):
+        toks = range(i * bs, min((i + 1) * bs, N))
+        qbar.append([sum(q[t][d] for t in toks) / len(toks) for d in range(D)])
+        for a in range(i * bs, i * bs + bs, w):
+            toks = range(a, min(a + w, (i + 1) * bs, N))
+            if len(toks):
+                parts.append((i, [sum(k[t][d] for t in toks) / len(toks) for d in range(D)]))
+    lg = O.hierarchical_logits(q, k, bs, g, scale)
+    for i in range(nb):
+        sub = [scale * sum(qbar[i][d] * kb[d] for d in range(D)) for _, kb in parts]
+        m = max(sub)
+        e = [math.exp(x - m) for x in sub]
+        tot = sum(e)
+        want = [0.0] * nb
+        for (j, _), x in zip(parts, e):
+            want[j] += x / tot
+        got = np.exp(lg[i] - lg[i].max())
+        got /= got.sum()
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
