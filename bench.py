@@ -300,6 +300,24 @@ def main(argv=None) -> int:
                "entries_out": int(cand_out.row_ptr[-1].item())}
         del cand_out
 
+    # Hierarchical block scoring (block logits over 4 key sub-blocks), timed on
+    # its own at the step's threshold.
+    hier_g = 4
+    ws_h = torch.empty(bsa.bsa_workspace_size(shape, 5, 0), dtype=torch.uint8, device=dev)
+    hier_out = bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int32,
+                                                                                       device=dev))
+    bsa.bsa_estimate_mask(q, k, top_p, w.block, keep_prefix_tokens=w.keep_prefix_tokens, out=hier_out,
+                          workspace=ws_h, sub_blocks=hier_g)
+    s0.record(stream)
+    for _ in range(nsel):
+        bsa.bsa_estimate_mask(q, k, top_p, w.block, keep_prefix_tokens=w.keep_prefix_tokens, out=hier_out,
+                              workspace=ws_h, sub_blocks=hier_g)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    hier = {"ms": round(s0.elapsed_time(s1) / nsel, 4), "sub_blocks": hier_g, "top_p": top_p,
+            "entries_out": int(hier_out.row_ptr[-1].item())}
+    del hier_out, ws_h
+
     # Token permutation (space-filling-curve order in for Q, K, V; the inverse
     # order out for O), timed on its own: an HBM-streaming gather/scatter.
     from workloads.hilbert import hilbert_order
@@ -386,6 +404,9 @@ def main(argv=None) -> int:
         red_bytes = 2.0 * w.B * w.H * w.N * w.D * 2 + 8.0 * (R + 1) + 4.0 * nnz + 4.0 * red["entries_out"]
         red["gbps"] = round(red_bytes / (red["ms"] * 1e-3) / 1e9, 1)
         out["estimator_reduced_search"] = red
+    hier_bytes = 2.0 * w.B * w.H * w.N * w.D * 2 + 4.0 * (R + 1) + 4.0 * hier["entries_out"]
+    hier["gbps"] = round(hier_bytes / (hier["ms"] * 1e-3) / 1e9, 1)
+    out["estimator_hierarchical"] = hier
     out["permute_tokens"] = {"ms": round(perm_ms, 4), "tensors": "gather q, k, v + scatter o",
                              "bytes": perm_bytes, "gbps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
                              "pct_hbm_peak": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}

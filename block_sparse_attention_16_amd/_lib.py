@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "bsa.h")
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
 BSA_BF16, BSA_FP32 = 0, 1
 BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_BACKWARD, BSA_WS_SELECT_FROM_MASS, BSA_WS_STRUCTURED = 0, 1, 2, 3, 4
+BSA_WS_ESTIMATE_HIER = 5
 (BSA_PATTERN_DENSE, BSA_PATTERN_SPATIAL, BSA_PATTERN_TEMPORAL, BSA_PATTERN_DIAGONAL, BSA_PATTERN_MULTI_DIAGONAL,
  BSA_PATTERN_STRIPES) = range(6)
 
@@ -58,6 +59,9 @@ def load() -> ctypes.CDLL:
     L.bsa_workspace_size.restype = sz
     L.bsa_estimate_mask.argtypes = [P(BsaShape), vp, vp, f32, f32, P(BsaCsr), i32, P(BsaCsr), vp, sz, vp]
     L.bsa_estimate_mask.restype = i32
+    L.bsa_estimate_mask_hierarchical.argtypes = [P(BsaShape), vp, vp, f32, f32, P(BsaCsr), i32, i32, P(BsaCsr), vp,
+                                                 sz, vp]
+    L.bsa_estimate_mask_hierarchical.restype = i32
     L.bsa_select_from_mass.argtypes = [P(BsaShape), P(BsaCsr), vp, f32, i32, P(BsaCsr), vp, sz, vp]
     L.bsa_select_from_mass.restype = i32
     L.bsa_structured_mask.argtypes = [P(BsaShape), vp, P(BsaPatternParams), P(BsaCsr), vp, sz, vp]

@@ -12,7 +12,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_FORWARD, BSA_WS_SELECT_FROM_MASS,
+from ._lib import (BSA_BF16, BSA_FP32, BSA_WS_BACKWARD, BSA_WS_ESTIMATE, BSA_WS_ESTIMATE_HIER, BSA_WS_FORWARD,
+                   BSA_WS_SELECT_FROM_MASS,
                    BSA_WS_STRUCTURED, BsaCsr, BsaPatternParams, BsaShape,
                    check, load)
 
@@ -106,8 +107,12 @@ def num_rows(q: torch.Tensor, block: int) -> int:
 
 def bsa_estimate_mask(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int, scale: float = 0.0,
                       candidate: Csr | None = None, keep_prefix_tokens: int = 0, out: Csr | None = None,
-                      capacity: int | None = None, workspace: torch.Tensor | None = None) -> Csr:
-    """Block-importance estimator -> CSR mask (see bsa_estimate_mask in include/bsa.h)."""
+                      capacity: int | None = None, workspace: torch.Tensor | None = None,
+                      sub_blocks: int = 1) -> Csr:
+    """Block-importance estimator -> CSR mask (see bsa_estimate_mask in include/bsa.h).
+    ``sub_blocks`` > 1 selects hierarchical block scoring
+    (bsa_estimate_mask_hierarchical): block logits as the log-sum-exp over
+    that many key sub-blocks."""
     _check(q, "q")
     _check(k, "k", like=q)
     shape = _shape_of(q, block)
@@ -117,12 +122,20 @@ def bsa_estimate_mask(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int
         cap = R * nb if capacity is None else capacity
         out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
                   torch.empty(cap, dtype=torch.int32, device=q.device))
-    ws = _workspace(shape, BSA_WS_ESTIMATE, 0, workspace, q.device)
     cand = ctypes.byref(candidate.c()) if candidate is not None else None
     oc = out.c()
-    st = load().bsa_estimate_mask(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p), float(scale), cand,
-                                  int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(), _stream())
-    check(st, "bsa_estimate_mask")
+    if sub_blocks == 1:
+        ws = _workspace(shape, BSA_WS_ESTIMATE, 0, workspace, q.device)
+        st = load().bsa_estimate_mask(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p), float(scale),
+                                      cand, int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(),
+                                      _stream())
+        check(st, "bsa_estimate_mask")
+    else:
+        ws = _workspace(shape, BSA_WS_ESTIMATE_HIER, 0, workspace, q.device)
+        st = load().bsa_estimate_mask_hierarchical(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p),
+                                                   float(scale), cand, int(keep_prefix_tokens), int(sub_blocks),
+                                                   ctypes.byref(oc), ws.data_ptr(), ws.numel(), _stream())
+        check(st, "bsa_estimate_mask_hierarchical")
     return out
 
 

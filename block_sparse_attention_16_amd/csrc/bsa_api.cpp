@@ -12,6 +12,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+constexpr int kMaxSubBlocks = 8;   // hierarchical block scoring: sub-blocks per key block
 
 bsa_status fail(bsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 bsa_status fail(bsa_status st, const char* fmt, ...) {
@@ -82,7 +83,8 @@ size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity
   if (make_problem(shape, &p) != BSA_OK || capacity < 0) return 0;
   size_t bytes = 0;
   switch (kind) {
-    case BSA_WS_ESTIMATE: bsa::carve_estimate(p, nullptr, &bytes); break;
+    case BSA_WS_ESTIMATE: bsa::carve_estimate(p, 1, nullptr, &bytes); break;
+    case BSA_WS_ESTIMATE_HIER: bsa::carve_estimate(p, kMaxSubBlocks, nullptr, &bytes); break;
     case BSA_WS_FORWARD: bsa::carve_forward(p, capacity, true, nullptr, &bytes); break;
     case BSA_WS_BACKWARD: bsa::carve_backward(p, capacity, nullptr, &bytes); break;
     case BSA_WS_SELECT_FROM_MASS:
@@ -92,9 +94,9 @@ size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity
   return bytes;
 }
 
-bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* k, float top_p, float scale,
-                             const bsa_csr* candidate, int32_t keep_prefix_tokens, bsa_csr* out, void* ws,
-                             size_t ws_bytes, void* stream) {
+static bsa_status estimate_common(const bsa_shape* shape, const void* q, const void* k, float top_p, float scale,
+                                  const bsa_csr* candidate, int32_t keep_prefix_tokens, int32_t sub_blocks,
+                                  bsa_csr* out, void* ws, size_t ws_bytes, void* stream, size_t need_for) {
   g_err[0] = 0;
   bsa::Problem p;
   BSA_TRY(make_problem(shape, &p));
@@ -104,6 +106,8 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
   if (!std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is not finite");
   if (keep_prefix_tokens < 0 || keep_prefix_tokens > p.N)
     return fail(BSA_ERR_INVALID_ARG, "keep_prefix_tokens=%d is outside [0, N]", keep_prefix_tokens);
+  if (sub_blocks != 1 && sub_blocks != 2 && sub_blocks != 4 && sub_blocks != 8)
+    return fail(BSA_ERR_INVALID_ARG, "sub_blocks=%d is not 1, 2, 4 or 8", sub_blocks);
   BSA_TRY(check_csr(out, "out"));
   if (candidate) {
     BSA_TRY(check_csr(candidate, "candidate"));
@@ -111,13 +115,27 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
       return fail(BSA_ERR_INVALID_ARG, "candidate aliases out");
   }
   size_t need = 0;
-  bsa::carve_estimate(p, nullptr, &need);
+  bsa::carve_estimate(p, (int)need_for, nullptr, &need);
   if (ws_bytes < need || (need && !ws))
     return fail(BSA_ERR_WORKSPACE, "estimate workspace needs %zu bytes, got %zu", need, ws_bytes);
-  bsa::EstimateWs w = bsa::carve_estimate(p, ws, &need);
+  bsa::EstimateWs w = bsa::carve_estimate(p, (int)need_for, ws, &need);
   return hip_status(bsa::launch_estimate(p, q, k, top_p, resolve_scale(scale, p.D), candidate, keep_prefix_tokens,
-                                         out, w, static_cast<hipStream_t>(stream)),
+                                         sub_blocks, out, w, static_cast<hipStream_t>(stream)),
                     "estimate launch");
+}
+
+bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* k, float top_p, float scale,
+                             const bsa_csr* candidate, int32_t keep_prefix_tokens, bsa_csr* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return estimate_common(shape, q, k, top_p, scale, candidate, keep_prefix_tokens, 1, out, ws, ws_bytes, stream, 1);
+}
+
+bsa_status bsa_estimate_mask_hierarchical(const bsa_shape* shape, const void* q, const void* k, float top_p,
+                                          float scale, const bsa_csr* candidate, int32_t keep_prefix_tokens,
+                                          int32_t sub_blocks, bsa_csr* out, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  return estimate_common(shape, q, k, top_p, scale, candidate, keep_prefix_tokens, sub_blocks, out, ws, ws_bytes,
+                         stream, kMaxSubBlocks);
 }
 
 bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass, float top_p,

@@ -35,15 +35,16 @@ struct Carver {
 // ---- estimator (estimate.hip) ----
 struct EstimateWs {
   float* qbar;       // [R, D] pooled query means
-  float* kbar;       // [R, D] pooled key means
+  float* kbar;       // [R * sub_blocks, D] pooled key means (per sub-block)
   int32_t* counts;   // [R] selected blocks per row
   uint32_t* bits;    // [R, words] selection bitmask
   float* logits;     // [R, nb] pooled logits
   int words;         // ceil(nb / 32)
 };
-EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes);
+EstimateWs carve_estimate(const Problem& p, int sub_blocks, void* ws, size_t* bytes);
+// sub_blocks: 1 (mean-pool logits) or 2, 4, 8 (hierarchical block scoring)
 hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
-                           const bsa_csr* cand, int keep_prefix_tokens, const bsa_csr* out,
+                           const bsa_csr* cand, int keep_prefix_tokens, int sub_blocks, const bsa_csr* out,
                            const EstimateWs& w, hipStream_t s);
 
 // ---- mask narrowing from block masses (estimate.hip) ----

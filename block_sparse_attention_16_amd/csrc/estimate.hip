@@ -7,9 +7,13 @@
 // search", GSRS page, Abstract and Figure 4 caption).
 //
 // Kernels, in launch order:
-//   pool_kernel     HBM-streaming mean of Q and K over every token block
+//   pool_kernel     HBM-streaming mean of Q and K over every token block (K
+//                   also per sub-block for hierarchical block scoring)
 //   logits_kernel   pooled logits scale * Qbar Kbar^T per head, an fp32 GEMM
-//                   on the matrix cores in 64 x 64 tiles
+//                   on the matrix cores in 64 x 64 tiles; with sub-blocks, a
+//                   block's logit is the log-sum-exp of its sub-blocks' (the
+//                   reading of the DFSAttn page's hierarchical block scoring,
+//                   Abstract)
 //   select_kernel   one wavefront per row: softmax over the row's candidates,
 //                   Top-p cut found by bisection on the ordered logit bits
 //                   (no sort), ties at the cut broken by lower block id,
@@ -61,39 +65,49 @@ struct Load8<float> {
   }
 };
 
-// Mean over the valid tokens of one block, for Q and K at once.
-// grid.x = R (one workgroup per (b, h, block)); 256 threads.
-// Thread t reads the 8-element chunk (t % (D/8)) of rows t/(D/8), +G, ...
-// A full block (the common case) issues all of a thread's loads before
-// summing any, so that 16-32 of them are in flight per thread.
-template <class T, int D, int BS>
+// Mean over the valid tokens of one block, for Q and K at once; K also per
+// sub-block when GS > 1 (GS sub-blocks of BS / GS tokens, for hierarchical
+// block scoring).  grid.x = rows from r0 (one workgroup per (b, h, block));
+// 256 threads.  Thread t reads the 8-element chunk (t % (D/8)) of G = 256 /
+// (D/8) row groups; row group g serves sub-block m = g % GS, rows
+// m * BS/GS + g / GS + it * G/GS, so each thread's K rows stay in one
+// sub-block (GS = 1: rows g, g + G, ...).  A full block (the common case)
+// issues all of a thread's loads before summing any.
+template <class T, int D, int BS, int GS>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                         float* __restrict__ qbar, float* __restrict__ kbar,
-                                                        int N, int nb) {
+                                                        int N, int nb, int r0) {
   constexpr int CPR = D / 8;            // chunks per row
   constexpr int G = kThreads / CPR;     // row groups
-  constexpr int ITER = BS / G;          // rows per thread in a full block
+  constexpr int GG = G / GS;            // row groups per sub-block
+  constexpr int W = BS / GS;            // rows per sub-block
+  constexpr int ITER = W / GG;          // rows per thread in a full block (= BS / G)
+  static_assert(GS <= G && W % GG == 0, "sub-blocks must split over the row groups");
   __shared__ float part[2][G][D];
-  const int r = blockIdx.x;             // = bh * nb + i
+  const int r = r0 + blockIdx.x;        // = bh * nb + i
   const int bh = r / nb, i = r - bh * nb;
   const int lo = i * BS;
   const int nv = min(BS, N - lo);
   const int c = threadIdx.x % CPR, g = threadIdx.x / CPR;
+  const int m = g % GS, gg = g / GS;
+  const int t0 = m * W + gg;            // first row of this thread; then + GG per step
   float sq[8] = {}, sk[8] = {};
   const size_t base = ((size_t)bh * N + lo) * D + c * 8;
   if (nv == BS) {
     float a[ITER][8], b[ITER][8];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      Load8<T>::get(q + base + (size_t)(g + it * G) * D, a[it]);
-      Load8<T>::get(k + base + (size_t)(g + it * G) * D, b[it]);
+      Load8<T>::get(q + base + (size_t)(t0 + it * GG) * D, a[it]);
+      Load8<T>::get(k + base + (size_t)(t0 + it * GG) * D, b[it]);
     }
 #pragma unroll
     for (int it = 0; it < ITER; ++it)
 #pragma unroll
       for (int e = 0; e < 8; ++e) { sq[e] += a[it][e]; sk[e] += b[it][e]; }
   } else {
-    for (int t = g; t < nv; t += G) {
+    for (int it = 0; it < ITER; ++it) {
+      const int t = t0 + it * GG;
+      if (t >= nv) break;               // rows of a sub-block ascend with it
       float a[8], b[8];
       Load8<T>::get(q + base + (size_t)t * D, a);
       Load8<T>::get(k + base + (size_t)t * D, b);
@@ -104,12 +118,18 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ q,
 #pragma unroll
   for (int e = 0; e < 8; ++e) { part[0][g][c * 8 + e] = sq[e]; part[1][g][c * 8 + e] = sk[e]; }
   __syncthreads();
-  if (threadIdx.x < 2 * D) {
-    const int which = threadIdx.x / D, d = threadIdx.x % D;
-    float s = 0.f;
-    for (int gg = 0; gg < G; ++gg) s += part[which][gg][d];
-    float* dst = which ? kbar : qbar;
-    dst[(size_t)r * D + d] = s / (float)nv;
+  for (int x = threadIdx.x; x < D + GS * D; x += kThreads) {
+    if (x < D) {
+      float s = 0.f;
+      for (int g2 = 0; g2 < G; ++g2) s += part[0][g2][x];
+      qbar[(size_t)r * D + x] = s / (float)nv;
+    } else {
+      const int ms = (x - D) / D, d = (x - D) % D;
+      const int cnt = max(0, min(W, nv - ms * W));
+      float s = 0.f;
+      for (int g2 = 0; g2 < GG; ++g2) s += part[1][g2 * GS + ms][d];
+      kbar[((size_t)r * GS + ms) * D + d] = cnt > 0 ? s / (float)cnt : 0.f;
+    }
   }
 }
 
@@ -125,27 +145,32 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
 // of one head on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32
 // products, fp32 accumulation, twice the rate of the vector FMA path).  256
 // threads; wave w computes the 32 x 32 sub-tile (w / 2, w % 2), d summed in
-// ascending pairs.  grid (ceil(nb/64), ceil(nb/64), B*H).
+// ascending pairs.  With GS > 1 the 64 columns are key sub-blocks (GS per
+// block) and the epilogue writes each block's logit as the natural
+// log-sum-exp of its non-empty sub-blocks' logits (GS consecutive lanes).
+// grid (ceil(nb * GS / 64), ceil(nb / 64), heads from bh0).
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-template <int D>
+template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar,
-                                                          float* __restrict__ logits, int nb, float scale) {
+                                                          float* __restrict__ logits, int nb, float scale,
+                                                          int bh0, int N, int bs) {
   constexpr int DC = 32;                  // d chunk staged in LDS, transposed to [d][row]
   __shared__ __attribute__((aligned(16))) float qs[DC][68];
   __shared__ __attribute__((aligned(16))) float ks[DC][68];
-  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
+  const int nk = nb * GS;                 // key columns (blocks or sub-blocks)
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = bh0 + blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
   const int l32 = lane & 31, hi = lane >> 5;
   const float* qh = qbar + (size_t)bh * nb * D;
-  const float* kh = kbar + (size_t)bh * nb * D;
+  const float* kh = kbar + (size_t)bh * nk * D;
   floatx16 acc = {};
   for (int d0 = 0; d0 < D; d0 += DC) {
     for (int x = tid; x < 64 * DC; x += kThreads) {
       const int row = x / DC, d = x % DC;
       qs[d][row] = i0 + row < nb ? qh[(size_t)(i0 + row) * D + d0 + d] : 0.f;
-      ks[d][row] = j0 + row < nb ? kh[(size_t)(j0 + row) * D + d0 + d] : 0.f;
+      ks[d][row] = j0 + row < nk ? kh[(size_t)(j0 + row) * D + d0 + d] : 0.f;
     }
     __syncthreads();
     // A[m][k] = Qbar[wi + m][d0 + kk + k] from lane m + 32k; B[k][n] = Kbar[wj + n][d0 + kk + k]
@@ -155,11 +180,28 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
     __syncthreads();
   }
   // accumulator element v of lane l: row 8(v/4) + 4(l/32) + v%4, column l%32
-  const int j = j0 + wj + l32;
+  const int jc = j0 + wj + l32;
+  if constexpr (GS == 1) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = i0 + wi + 8 * (v >> 2) + 4 * hi + (v & 3);
-    if (i < nb && j < nb) logits[((size_t)bh * nb + i) * nb + j] = acc[v] * scale;
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + wi + 8 * (v >> 2) + 4 * hi + (v & 3);
+      if (i < nb && jc < nb) logits[((size_t)bh * nb + i) * nb + jc] = acc[v] * scale;
+    }
+  } else {
+    const int jb = jc / GS, ms = jc % GS;
+    const bool live = jc < nk && jb * bs + ms * (bs / GS) < N;   // sub-block holds a token
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float x = live ? acc[v] * scale : -INFINITY;
+      float mx = x;
+#pragma unroll
+      for (int off = 1; off < GS; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      float e = live ? expf(x - mx) : 0.f;
+#pragma unroll
+      for (int off = 1; off < GS; off <<= 1) e += __shfl_xor(e, off);
+      const int i = i0 + wi + 8 * (v >> 2) + 4 * hi + (v & 3);
+      if (ms == 0 && i < nb && jb < nb) logits[((size_t)bh * nb + i) * nb + jb] = mx + logf(e);
+    }
   }
 }
 
@@ -627,12 +669,12 @@ __global__ __launch_bounds__(kThreads) void pattern_kernel(const int32_t* __rest
 
 }  // namespace
 
-EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes) {
+EstimateWs carve_estimate(const Problem& p, int sub_blocks, void* ws, size_t* bytes) {
   Carver c(ws);
   EstimateWs w;
   w.words = (p.nb + 31) / 32;
   w.qbar = c.take<float>((size_t)p.R * p.D);
-  w.kbar = c.take<float>((size_t)p.R * p.D);
+  w.kbar = c.take<float>((size_t)p.R * sub_blocks * p.D);
   w.counts = c.take<int32_t>((size_t)p.R);
   w.bits = c.take<uint32_t>((size_t)p.R * w.words);
   w.logits = c.take<float>((size_t)p.R * p.nb);
@@ -640,17 +682,28 @@ EstimateWs carve_estimate(const Problem& p, void* ws, size_t* bytes) {
   return w;
 }
 
-template <class T, int D>
+template <class T, int D, int GS>
 static void launch_pool_logits(const Problem& p, const void* q, const void* k, float scale, const EstimateWs& w,
                                hipStream_t s) {
   if (p.bs == 128)
-    pool_kernel<T, D, 128><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
-                                                    w.kbar, p.N, p.nb);
+    pool_kernel<T, D, 128, GS><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
+                                                        w.kbar, p.N, p.nb, 0);
   else
-    pool_kernel<T, D, 64><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
-                                                   w.kbar, p.N, p.nb);
-  const dim3 g((p.nb + 63) / 64, (p.nb + 63) / 64, p.B * p.H);
-  logits_kernel<D><<<g, kThreads, 0, s>>>(w.qbar, w.kbar, w.logits, p.nb, scale);
+    pool_kernel<T, D, 64, GS><<<p.R, kThreads, 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k), w.qbar,
+                                                       w.kbar, p.N, p.nb, 0);
+  const dim3 g((p.nb * GS + 63) / 64, (p.nb + 63) / 64, p.B * p.H);
+  logits_kernel<D, GS><<<g, kThreads, 0, s>>>(w.qbar, w.kbar, w.logits, p.nb, scale, 0, p.N, p.bs);
+}
+
+template <class T, int D>
+static void launch_pool_logits_gs(const Problem& p, const void* q, const void* k, float scale, int sub_blocks,
+                                  const EstimateWs& w, hipStream_t s) {
+  switch (sub_blocks) {
+    case 1: launch_pool_logits<T, D, 1>(p, q, k, scale, w, s); break;
+    case 2: launch_pool_logits<T, D, 2>(p, q, k, scale, w, s); break;
+    case 4: launch_pool_logits<T, D, 4>(p, q, k, scale, w, s); break;
+    default: launch_pool_logits<T, D, 8>(p, q, k, scale, w, s); break;
+  }
 }
 
 template <int EPL, bool FROM_MASS>
@@ -677,16 +730,16 @@ static void launch_csr(const Problem& p, const int32_t* counts, const uint32_t* 
 }
 
 hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
-                           const bsa_csr* cand, int keep_prefix_tokens, const bsa_csr* out, const EstimateWs& w,
-                           hipStream_t s) {
+                           const bsa_csr* cand, int keep_prefix_tokens, int sub_blocks, const bsa_csr* out,
+                           const EstimateWs& w, hipStream_t s) {
   const int n_forced = min(p.nb, (keep_prefix_tokens + p.bs - 1) / p.bs);
   const bool bf = p.dtype == BSA_BF16;
   if (p.D == 64) {
-    if (bf) launch_pool_logits<__bf16, 64>(p, q, k, scale, w, s);
-    else launch_pool_logits<float, 64>(p, q, k, scale, w, s);
+    if (bf) launch_pool_logits_gs<__bf16, 64>(p, q, k, scale, sub_blocks, w, s);
+    else launch_pool_logits_gs<float, 64>(p, q, k, scale, sub_blocks, w, s);
   } else {
-    if (bf) launch_pool_logits<__bf16, 128>(p, q, k, scale, w, s);
-    else launch_pool_logits<float, 128>(p, q, k, scale, w, s);
+    if (bf) launch_pool_logits_gs<__bf16, 128>(p, q, k, scale, sub_blocks, w, s);
+    else launch_pool_logits_gs<float, 128>(p, q, k, scale, sub_blocks, w, s);
   }
   if (cand) {
     launch_select_any<false>(p, w.logits, top_p, cand, n_forced, w.counts, w.bits, w.words, s);

@@ -83,7 +83,8 @@ typedef enum {
   BSA_WS_FORWARD = 1,
   BSA_WS_BACKWARD = 2,
   BSA_WS_SELECT_FROM_MASS = 3,
-  BSA_WS_STRUCTURED = 4
+  BSA_WS_STRUCTURED = 4,
+  BSA_WS_ESTIMATE_HIER = 5    /* bsa_estimate_mask_hierarchical, any sub_blocks */
 } bsa_ws_kind;
 
 /* Bytes of device workspace `kind` needs for `shape` and a CSR of `capacity`
@@ -113,6 +114,26 @@ bsa_status bsa_estimate_mask(const bsa_shape* shape, const void* q, const void* 
                              float top_p, float scale, const bsa_csr* candidate,
                              int32_t keep_prefix_tokens, bsa_csr* out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Hierarchical block scoring.  The DFSAttn page (Abstract) names hierarchical
+ * block scoring for block importance without defining it; this library reads
+ * it as: each key block j splits into sub_blocks sub-blocks of
+ * block / sub_blocks tokens (sub-blocks past N are left out), the query block
+ * mean is scored against each sub-block mean, scale * <Qbar_i, Kbar_{j,m}>,
+ * and block j's logit is the natural log-sum-exp over its sub-blocks.  A
+ * block's softmax probability is then the sum of its sub-blocks'
+ * probabilities, so one strongly matched sub-block (a vertical stripe, a
+ * small object) is not averaged away.  Softmax, Top-p, ranking, candidates,
+ * forced blocks and the output are those of bsa_estimate_mask.
+ *   sub_blocks 1, 2, 4 or 8 (1: the logits of bsa_estimate_mask).
+ *   ws         at least bsa_workspace_size(shape, BSA_WS_ESTIMATE_HIER, 0)
+ *              bytes (sized for 8 sub-blocks).
+ * Errors: BSA_ERR_INVALID_ARG for any other sub_blocks, otherwise as
+ * bsa_estimate_mask. */
+bsa_status bsa_estimate_mask_hierarchical(const bsa_shape* shape, const void* q, const void* k,
+                                          float top_p, float scale, const bsa_csr* candidate,
+                                          int32_t keep_prefix_tokens, int32_t sub_blocks,
+                                          bsa_csr* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Mask narrowing from exact block attention weights.  The GSRS page
  * (Abstract) obtains exact attention weights inside the attention computation

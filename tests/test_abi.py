@@ -26,7 +26,8 @@ def _csr(cap=1024):
 @needs_lib
 def test_library_exports_every_header_function():
     names = _lib.header_functions()
-    assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_forward", "bsa_last_error",
+    assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_estimate_mask_hierarchical", "bsa_forward",
+                            "bsa_last_error",
                             "bsa_permute_rows", "bsa_select_from_mass", "bsa_status_string", "bsa_structured_mask", "bsa_version",
                             "bsa_workspace_size"])
     L = _lib.load()
@@ -56,6 +57,8 @@ def test_workspace_sizes():
     assert fwd >= 100 * 64 * 4          # per-entry, per-query partial sums for the block mass
     sel = L.bsa_workspace_size(ctypes.byref(s), 3, 0)
     assert sel >= R * 4 + R * ((nb + 31) // 32) * 4      # counts + kept-block bitmask
+    hier = L.bsa_workspace_size(ctypes.byref(s), 5, 0)
+    assert hier >= L.bsa_workspace_size(ctypes.byref(s), 0, 0) + 7 * R * 64 * 4   # 8 key sub-block means per block
     assert L.bsa_workspace_size(ctypes.byref(_shape(D=96)), 0, 0) == 0
     assert L.bsa_workspace_size(ctypes.byref(s), 7, 0) == 0
 
@@ -91,6 +94,22 @@ def test_estimate_validation():
     assert _est(L, s, out=bad) == _lib.BSA_ERR_INVALID_ARG
     neg = _lib.BsaCsr(FAKE, FAKE, -1)
     assert _est(L, s, out=neg) == _lib.BSA_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_hierarchical_estimate_validation():
+    L = _lib.load()
+    s = _shape()
+    need = L.bsa_workspace_size(ctypes.byref(s), 5, 0)
+
+    def call(g, ws_bytes=1 << 30, p=0.9):
+        return L.bsa_estimate_mask_hierarchical(ctypes.byref(s), FAKE, FAKE, p, 0.0, None, 0, g,
+                                                ctypes.byref(_csr()), FAKE, ws_bytes, None)
+    for g in (0, 3, 16, -2):
+        assert call(g) == _lib.BSA_ERR_INVALID_ARG
+        assert b"sub_blocks" in L.bsa_last_error()
+    assert call(4, ws_bytes=need - 256) == _lib.BSA_ERR_WORKSPACE
+    assert call(4, p=0.0) == _lib.BSA_ERR_INVALID_ARG
 
 
 @needs_lib
