@@ -155,7 +155,11 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
                                                           const float* __restrict__ kbar,
                                                           float* __restrict__ logits, int nb, float scale,
                                                           int bh0, int N, int bs) {
-  constexpr int DC = 32;                  // d chunk staged in LDS, transposed to [d][row]
+  // 64 x DC slices of Qbar and Kbar go to LDS transposed to [d][row] (row
+  // padded to 68), every 16-byte load of a slice in flight before its
+  // stores; lanes cover 64 rows of one 4-wide d slice, so the transposed LDS
+  // writes are conflict free.  Then DC / 2 MFMAs per slice.
+  constexpr int DC = 32;   // 32: best of 32 / 64 / D measured (more resident workgroups)
   __shared__ __attribute__((aligned(16))) float qs[DC][68];
   __shared__ __attribute__((aligned(16))) float ks[DC][68];
   const int nk = nb * GS;                 // key columns (blocks or sub-blocks)
@@ -165,16 +169,29 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
   const int l32 = lane & 31, hi = lane >> 5;
   const float* qh = qbar + (size_t)bh * nb * D;
   const float* kh = kbar + (size_t)bh * nk * D;
+  constexpr int LOADS = 64 * DC / 4 / kThreads;  // float4 loads per thread, matrix and slice
   floatx16 acc = {};
   for (int d0 = 0; d0 < D; d0 += DC) {
-    for (int x = tid; x < 64 * DC; x += kThreads) {
-      const int row = x / DC, d = x % DC;
-      qs[d][row] = i0 + row < nb ? qh[(size_t)(i0 + row) * D + d0 + d] : 0.f;
-      ks[d][row] = j0 + row < nk ? kh[(size_t)(j0 + row) * D + d0 + d] : 0.f;
+    float4 qa[LOADS], ka[LOADS];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int x = tid + it * kThreads, row = x & 63, c4 = x >> 6;
+      qa[it] = i0 + row < nb ? *reinterpret_cast<const float4*>(qh + (size_t)(i0 + row) * D + d0 + 4 * c4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      ka[it] = j0 + row < nk ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + row) * D + d0 + 4 * c4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int x = tid + it * kThreads, row = x & 63, c4 = x >> 6;
+      qs[4 * c4][row] = qa[it].x; qs[4 * c4 + 1][row] = qa[it].y;
+      qs[4 * c4 + 2][row] = qa[it].z; qs[4 * c4 + 3][row] = qa[it].w;
+      ks[4 * c4][row] = ka[it].x; ks[4 * c4 + 1][row] = ka[it].y;
+      ks[4 * c4 + 2][row] = ka[it].z; ks[4 * c4 + 3][row] = ka[it].w;
     }
     __syncthreads();
     // A[m][k] = Qbar[wi + m][d0 + kk + k] from lane m + 32k; B[k][n] = Kbar[wj + n][d0 + kk + k]
-#pragma unroll
+#pragma unroll 8
     for (int kk = 0; kk < DC; kk += 2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[kk + hi][wi + l32], ks[kk + hi][wj + l32], acc, 0, 0, 0);
     __syncthreads();
