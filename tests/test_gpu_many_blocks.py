@@ -74,3 +74,29 @@ def test_hierarchical_many_blocks(bsa):
     _, _, sels = O.estimate_mask(q, k, bs, p, default_scale(D), sub_blocks=g)
     rows, bad, band = compare_masks(rp, ci, sels, 1, O.num_blocks(N, bs), p)
     assert not bad, f"{len(bad)} of {rows} rows differ outside the band"
+
+
+@pytest.mark.parametrize("delta", ["exact", "o32"])
+def test_backward_many_blocks(bsa, delta):
+    # 1100 key blocks per head: the CSC transpose and the dK/dV grid's
+    # longest-first tail at a wide mask; a sparse random mask keeps the
+    # oracle's gradients quick
+    from tests.gpu_helpers import compare_backward
+    bs, D, N = 64, 64, 1100 * 64 - 23
+    nb = O.num_blocks(N, bs)
+    q, k, v = _qkv(11, N, D)
+    rng = np.random.default_rng(12)
+    g = round_to_bf16(rng.normal(size=q.shape).astype(np.float32))
+    rows = [np.zeros(0, np.int64) if r % 9 == 4 else
+            np.sort(rng.choice(nb, size=int(rng.integers(1, 40)), replace=False)) for r in range(nb)]
+    rows[nb - 1] = np.arange(nb - 30, nb)                  # the ragged last block in its own row
+    rp, ci = O.rows_to_csr(rows)
+    mask = bsa.csr_from_host(rp, ci, "cuda")
+    qd, kd, vd, gd = (to_device(t, "bf16") for t in (q, k, v, g))
+    o32 = torch.empty(qd.shape, dtype=torch.float32, device="cuda") if delta == "o32" else None
+    o, lse, _ = bsa.bsa_forward(qd, kd, vd, mask, bs, want_mass=False, o32=o32)
+    dq, dk, dv = bsa.bsa_backward(qd, kd, vd, o, gd, lse, mask, bs, o32=o32)
+    torch.cuda.synchronize()
+    err = compare_backward({"q": q, "k": k, "v": v, "g": g}, bs, rp, ci, default_scale(D), [(0, 0)],
+                           {"dq": to_host(dq), "dk": to_host(dk), "dv": to_host(dv)}, "bf16")
+    assert err["excess"] <= 0.0, f"gradient errors {err}"
