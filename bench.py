@@ -177,8 +177,8 @@ def main(argv=None) -> int:
                          "(reference point for HBM byte counters under rocprofv3 --pmc)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards over heads "
-                                   "with no exchange, but no multi-GPU run is part of it)"}))
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1 (the path shards over "
+                                   "heads with no exchange, and no multi-GPU run is implemented)"}))
         return 2
 
     import torch
