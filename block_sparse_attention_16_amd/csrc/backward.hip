@@ -26,12 +26,15 @@
 // column and 16 rows {8a + 4h + r}, and the k-slot permutation that lets an
 // accumulator, rounded to bf16, feed the next MFMA as its B operand.
 //
-// Like the forward, both MFMA kernels walk their blocks in units of SUB rows
-// of the streamed operand, double-buffered in LDS and filled with buffer
-// loads straight into LDS (exact LDS wait counts while a copy is in flight;
-// reads past the end return zeros); block ids come one unit ahead through
+// Like the forward, both MFMA kernels stream their operand through LDS with
+// buffer loads straight into LDS (exact LDS wait counts while a copy is in
+// flight; reads past the end return zeros); block ids come ahead through
 // vector loads; operand reads run ahead of the MFMAs under scheduling fences.
-// Units are small enough for two waves per SIMD.
+// dq_kernel double-buffers units of SUB keys at two waves per SIMD.
+// dkv_kernel streams 32-query tiles through three LDS slots and is
+// software-pipelined one tile deep (at D = 128 its registers allow one wave
+// per SIMD, so its VALU work must run under its own MFMAs).  Both grids
+// dispatch their last rows longest first (order.hip).
 #include <type_traits>
 
 #include "bsa_internal.h"

@@ -14,10 +14,13 @@
 //                   block's logit is the log-sum-exp of its sub-blocks' (the
 //                   reading of the DFSAttn page's hierarchical block scoring,
 //                   Abstract)
-//   select_kernel   one wavefront per row: softmax over the row's candidates,
-//                   Top-p cut found by bisection on the ordered logit bits
-//                   (no sort), ties at the cut broken by lower block id,
-//                   forced prefix blocks -> selection bitmask
+//   select_full_kernel  (every block a candidate) one wavefront per row:
+//                   softmax over the row, Top-p cut found by bisection on the
+//                   ordered logit bits (no sort), ties at the cut broken by
+//                   lower block id, forced prefix blocks; the selection of
+//                   64 blocks is one ballot -> selection bitmask
+//   select_kernel   the same rule over each row's candidate blocks (reduced
+//                   search) -> selection bitmask
 //   scan_kernel     exclusive scan of the per-row counts -> CSR row_ptr
 //   compact_kernel  one wavefront per row: bitmask -> ascending col_idx
 //
