@@ -19,7 +19,7 @@ namespace {
 template <int VEC>
 struct Vec;
 template <>
-struct Vec<16> { using T = uint4; };
+struct Vec<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
 template <>
 struct Vec<4> { using T = uint32_t; };
 
@@ -27,20 +27,38 @@ template <int VEC, bool INVERSE>
 __global__ __launch_bounds__(256) void permute_kernel(const char* __restrict__ src, const int32_t* __restrict__ perm,
                                                       char* __restrict__ dst, int n, int upr, int total_units) {
   using T = typename Vec<VEC>::T;
+  constexpr int K = 4;                               // units per thread per step, loads before stores
   const int stride = gridDim.x * 256;
-  for (int u = blockIdx.x * 256 + threadIdx.x; u < total_units; u += stride) {
-    const int row = u / upr, c = u - row * upr;      // row = h * n + t
-    const int h = row / n, t = row - h * n;
-    const int p = perm[t];
-    const bool ok = p >= 0 && p < n;
-    const size_t other = ((size_t)h * n + (ok ? p : 0)) * upr + c;
-    if constexpr (!INVERSE) {
-      T v{};
-      if (ok) v = reinterpret_cast<const T*>(src)[other];
-      reinterpret_cast<T*>(dst)[u] = v;
-    } else {
-      if (ok) reinterpret_cast<T*>(dst)[other] = reinterpret_cast<const T*>(src)[u];
+  for (int u0 = blockIdx.x * 256 + threadIdx.x; u0 < total_units; u0 += K * stride) {
+    T v[K];
+    size_t to[K];
+    bool ok[K];
+#pragma unroll
+    for (int x = 0; x < K; ++x) {
+      const int u = u0 + x * stride;
+      ok[x] = false;
+      to[x] = 0;
+      v[x] = T{};
+      if (u < total_units) {
+        const int row = u / upr, c = u - row * upr;      // row = h * n + t
+        const int h = row / n, t = row - h * n;
+        const int p = perm[t];
+        const bool okp = p >= 0 && p < n;
+        const size_t other = ((size_t)h * n + (okp ? p : 0)) * upr + c;
+        if constexpr (!INVERSE) {
+          if (okp) v[x] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src) + other);
+          to[x] = (size_t)u;
+          ok[x] = true;
+        } else {
+          v[x] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src) + u);
+          to[x] = other;
+          ok[x] = okp;
+        }
+      }
     }
+#pragma unroll
+    for (int x = 0; x < K; ++x)
+      if (ok[x]) __builtin_nontemporal_store(v[x], reinterpret_cast<T*>(dst) + to[x]);
   }
 }
 
