@@ -49,6 +49,24 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
+ESTIMATOR_SOURCES = ["block_sparse_attention_16_amd/csrc/estimate.hip"]
+
+
+def load_estimator_traffic(workload: str):
+    """Counted HBM bytes of one estimator call (its five kernels) from the
+    committed rocprofv3 counter runs, if taken on the current estimator
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", "estimator_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != source_hash(ESTIMATOR_SOURCES):
+        return None
+    return entry.get("hbm_bytes_per_call")
+
+
 def load_traffic(kernel: str, workload: str, flop_per_launch: float):
     """HBM bytes per forward launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source; else None."""
@@ -364,6 +382,7 @@ def main(argv=None) -> int:
     fwd_tflops = exec_flop / (fwd_ms * 1e-3) / 1e12
     est_bytes = 2.0 * w.B * w.H * w.N * w.D * 2 + 4.0 * (R + 1) + 4.0 * nnz
     traffic = load_traffic("fwd_kernel", w.name, exec_flop)
+    est_counted = load_estimator_traffic(w.name)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -388,7 +407,9 @@ def main(argv=None) -> int:
                        "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
         "estimator": {"ms": round(est_ms, 4), "algorithmic_bytes": est_bytes,
                       "gbps": round(est_bytes / (est_ms * 1e-3) / 1e9, 1),
-                      "pct_hbm_peak": round(100 * est_bytes / (est_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)},
+                      "pct_hbm_peak": round(100 * est_bytes / (est_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                      "counted_bytes": est_counted,
+                      "counted_gbps": (round(est_counted / (est_ms * 1e-3) / 1e9, 1) if est_counted else None)},
         "block_density": nnz / (R * w.nb),
         "token_pair_density": pairs / (w.B * w.H * float(w.N) ** 2),
         "nnz": nnz,
