@@ -53,7 +53,7 @@ ESTIMATOR_SOURCES = ["block_sparse_attention_16_amd/csrc/estimate.hip"]
 
 
 def load_estimator_traffic(workload: str):
-    """Counted HBM bytes of one estimator call (its five kernels) from the
+    """Counted HBM bytes of one estimator call (its four kernels) from the
     committed rocprofv3 counter runs, if taken on the current estimator
     source; else None."""
     path = os.path.join(ROOT, "profiles", "estimator_traffic.json")

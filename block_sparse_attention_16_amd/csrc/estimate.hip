@@ -21,19 +21,20 @@
 //                   64 blocks is one ballot -> selection bitmask
 //   select_kernel   the same rule over each row's candidate blocks (reduced
 //                   search) -> selection bitmask
-//   scan_kernel     exclusive scan of the per-row counts -> CSR row_ptr
-//   compact_kernel  one wavefront per row: bitmask -> ascending col_idx
+//   csr_kernel      per workgroup of 32 rows: sum of the earlier rows' counts,
+//                   scan of its own -> CSR row_ptr; bitmasks -> ascending
+//                   col_idx (one wavefront per 8 rows, 64 blocks per store)
 //
 // Mask narrowing (GSRS page, Abstract and Figure 4 caption: exact attention
 // weights, later searches restricted to an earlier step's blocks) reuses
 // select_kernel in its FROM_MASS form -- the weights are a CSR row's block
-// masses instead of exp(logit - max) -- followed by the same scan and compact.
+// masses instead of exp(logit - max) -- followed by the same csr_kernel.
 //
 // Structured head masks (SVG page, Abstract: spatial and temporal heads;
 // Sparse-vDiT page, Abstract: diagonal, multi-diagonal and vertical-stripe
 // patterns): pattern_kernel evaluates the block relation of each row's head
 // with interval arithmetic on frames and spatial positions, into the same
-// bitmask, then the same scan and compact.
+// bitmask, then the same csr_kernel.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -270,6 +271,33 @@ __device__ __forceinline__ float uniform(float x) {
   return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
 
+// Early end of the bisection for the cut key.  Once bit b is decided the cut
+// lies in [T, T + 2^b) (T's lower bits are zero), with M(T) >= p Z and
+// M(T + 2^b) < p Z.  If exactly one present block's key x falls in that
+// range, M is constant on [T, x] and on (x, T + 2^b], so the cut is x.
+// Ballots count the blocks in range; the result is wave-uniform.  Tied keys
+// in range keep the bisection going.
+template <int EPL>
+__device__ __forceinline__ bool isolated_cut(const uint32_t (&key)[EPL], uint32_t T, int b, uint32_t& cut) {
+  int n = 0;
+  uint32_t kin = 0u;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const bool in = key[e] != 0u && (key[e] ^ T) < (1u << b);
+    n += __popcll(__ballot(in));
+    kin = in ? key[e] : kin;
+  }
+  if (n != 1) return false;
+  cut = __builtin_amdgcn_readfirstlane(wave_umax(kin));
+  return true;
+}
+// Bits after which the bisection tests for an isolated cut (steps 12, 16,
+// 20 and 24 of 32): on the video workloads' pooled logits the cut key is
+// alone in its range after 15-17 steps on average.
+__device__ __forceinline__ constexpr bool isolation_check(int bit) {
+  return bit == 20 || bit == 16 || bit == 12 || bit == 8;
+}
+
 // Full search (no candidate rows), one mask row per wavefront, 4 per
 // workgroup: lane l holds blocks j = 64e + l, e < EPL.  Same Top-p rule as
 // select_kernel below (bisection for the cut logit L*, blocks above it kept,
@@ -318,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void select_full_kernel(const float* __re
 #pragma unroll
       for (int e = 0; e < EPL; ++e) m += key[e] >= c ? ev[e] : 0.f;
       if (uniform(wave_sum(m)) >= thr) T = c;
+      if (isolation_check(bit) && isolated_cut<EPL>(key, T, bit, T)) break;
     }
     cut = T;                                 // L*: M(L*) >= p Z > M(L* + 1)
     int nt = 0;
@@ -458,6 +487,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) m += key[e] >= c ? ev[e] : 0.f;
       if (wave_sum(m) >= thr) T = c;
+      if (isolation_check(bit) && isolated_cut<EPL>(key, T, bit, T)) break;
     }
     cut = T;                                 // L*: M(L*) >= p Z > M(L* + 1)
     int nt = 0;
@@ -515,87 +545,100 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   if (lane == 0) counts[r] = cnt;
 }
 
-// Exclusive scan of counts[R] into row_ptr[R+1]: one workgroup of 1024
-// threads; per pass of 8192 rows each thread scans 8 consecutive counts in
-// registers, and one wave-and-workgroup scan of the thread totals gives the
-// offsets.  counts is workspace memory (16-byte aligned); row_ptr is the
-// caller's and is stored by dwords.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr,
-                                                    int R) {
-  __shared__ int wtot[16];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int carry = 0;
-  for (int base = 0; base < R; base += 8192) {
-    const int i0 = base + tid * 8;
-    int v[8];
-    if (i0 + 8 <= R) {
-      const int4 a = *reinterpret_cast<const int4*>(counts + i0);
-      const int4 b = *reinterpret_cast<const int4*>(counts + i0 + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = i0 + k < R ? counts[i0 + k] : 0;
-    }
-    int sum = 0;                      // v becomes the exclusive scan within the thread
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = v[k];
-      v[k] = sum;
-      sum += c;
-    }
-    int x = sum;                      // inclusive scan of the thread totals over the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) wtot[wid] = x;
-    __syncthreads();
-    int wbase = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int t = wtot[w];
-      wbase += w < wid ? t : 0;
-      total += t;
-    }
-    const int off = carry + wbase + x - sum;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (i0 + k < R) row_ptr[i0 + k] = off + v[k];
-    carry += total;
-    __syncthreads();                  // wtot is rewritten by the next pass
-  }
-  if (tid == 0) row_ptr[R] = carry;
+// CSR assembly in one launch.  Workgroup b takes rows [32b, 32b + 32): it sums
+// the counts of every earlier row (16-byte loads, wave and workgroup sums;
+// at most R counts, read from L2), scans its own 32 counts across lanes and
+// writes their row_ptr (and row_ptr[R]).  Then each wavefront writes 8 rows'
+// ids: for every 64 blocks of a row's bitmask (two words, uniform), lane l
+// stores block 64c + l at the row offset plus the number of set bits below
+// its own (mbcnt), so a row takes one masked store per 64 blocks.  Ids at
+// positions >= cap are dropped; row_ptr keeps the exact offsets.
+constexpr int kCsrRowsPerWave = 8;
+constexpr int kCsrRows = 4 * kCsrRowsPerWave;     // rows per workgroup (<= 64)
+
+// Blocks j0 .. j0 + 63 of one row, selected by the 64-bit mask (hi:lo),
+// written from position pos on in ascending order.
+__device__ __forceinline__ void emit64(uint32_t lo, uint32_t hi, int j0, int64_t pos, int32_t* __restrict__ col_idx,
+                                       int64_t cap, int lane) {
+  const uint32_t word = lane < 32 ? lo : hi;
+  const bool set = (word >> (lane & 31)) & 1u;
+  const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+  const int64_t at = pos + rank;
+  if (set && at < cap) col_idx[at] = j0 + lane;
 }
 
-// One wavefront per row: set bits -> ascending block ids at row_ptr[r].
-__global__ __launch_bounds__(kThreads) void compact_kernel(const uint32_t* __restrict__ bits,
-                                                           const int32_t* __restrict__ row_ptr,
-                                                           int32_t* __restrict__ col_idx, int64_t cap, int R,
-                                                           int words) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (r >= R) return;
-  int64_t pos_base = row_ptr[r];
-  for (int w0 = 0; w0 < words; w0 += 64) {
-    const int w = w0 + lane;
-    const uint32_t b = w < words ? bits[(size_t)r * words + w] : 0u;
-    const int pc = __popc(b);
-    int x = pc;
-    for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+__global__ __launch_bounds__(kThreads) void csr_kernel(const int32_t* __restrict__ counts,
+                                                       const uint32_t* __restrict__ bits,
+                                                       int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+                                                       int64_t cap, int R, int words) {
+  constexpr int RW = kCsrRowsPerWave;
+  __shared__ int wsum[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r0 = blockIdx.x * kCsrRows;            // a multiple of 4
+  int s = 0;
+  const int4* c4 = reinterpret_cast<const int4*>(counts);
+  const int n4 = r0 / 4;
+  int x = tid;
+  for (; x + 7 * kThreads < n4; x += 8 * kThreads) {   // eight 16-byte loads in flight per thread
+    int4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c4[x + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+  for (; x < n4; x += kThreads) {
+    const int4 v = c4[x];
+    s += v.x + v.y + v.z + v.w;
+  }
+  s = wave_sum_i(s);
+  if (lane == 0) wsum[wid] = s;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) base += wsum[w];
+  const int cx = (lane < kCsrRows && r0 + lane < R) ? counts[r0 + lane] : 0;
+  int inc = cx;                                    // inclusive scan over lanes
+#pragma unroll
+  for (int off = 1; off < kCsrRows; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  const int exc = inc - cx;                        // offset of row r0 + lane within the workgroup
+  if (wid == 0 && lane < kCsrRows && r0 + lane < R) {
+    row_ptr[r0 + lane] = base + exc;
+    if (r0 + lane == R - 1) row_ptr[R] = base + inc;
+  }
+  const int x0 = wid * RW;
+  if (words <= 64) {                               // a row's words in one load (lane w: word w), 8 rows at once
+    uint32_t bw[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      const int r = r0 + x0 + j;
+      bw[j] = (r < R && lane < words) ? bits[(size_t)r * words + lane] : 0u;
     }
-    int64_t pos = pos_base + x - pc;
-    uint32_t m = b;
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      if (pos >= 0 && pos < cap) col_idx[pos] = w * 32 + bit;
-      ++pos;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      int64_t pos = (int64_t)base + __builtin_amdgcn_readlane(exc, x0 + j);
+      for (int c = 0; c < words; c += 2) {
+        const uint32_t lo = __builtin_amdgcn_readlane(bw[j], c);
+        const uint32_t hi = c + 1 < words ? __builtin_amdgcn_readlane(bw[j], c + 1) : 0u;
+        emit64(lo, hi, c * 32, pos, col_idx, cap, lane);
+        pos += __popc(lo) + __popc(hi);
+      }
     }
-    pos_base += __shfl(x, 63);
+  } else {
+    for (int j = 0; j < RW; ++j) {
+      const int r = r0 + x0 + j;
+      if (r >= R) break;
+      int64_t pos = (int64_t)base + __builtin_amdgcn_readlane(exc, x0 + j);
+      const uint32_t* row = bits + (size_t)r * words;
+      for (int c = 0; c < words; c += 2) {
+        const uint32_t lo = row[c];
+        const uint32_t hi = c + 1 < words ? row[c + 1] : 0u;
+        emit64(lo, hi, c * 32, pos, col_idx, cap, lane);
+        pos += __popc(lo) + __popc(hi);
+      }
+    }
   }
 }
 
@@ -748,8 +791,8 @@ static void launch_select_any(const Problem& p, const float* vals, float top_p, 
 
 static void launch_csr(const Problem& p, const int32_t* counts, const uint32_t* bits, int words, const bsa_csr* out,
                        hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(counts, out->row_ptr, p.R);
-  compact_kernel<<<(p.R + 3) / 4, kThreads, 0, s>>>(bits, out->row_ptr, out->col_idx, out->capacity, p.R, words);
+  csr_kernel<<<(p.R + kCsrRows - 1) / kCsrRows, kThreads, 0, s>>>(counts, bits, out->row_ptr, out->col_idx,
+                                                                  out->capacity, p.R, words);
 }
 
 hipError_t launch_estimate(const Problem& p, const void* q, const void* k, float top_p, float scale,
