@@ -23,7 +23,18 @@
 // loop is software-pipelined by one unit inside each wave: while the matrix
 // cores compute the scores of unit u+1, the VALU turns the scores of unit u
 // into probabilities; while they accumulate unit u's P V, the VALU takes the
-// row max of unit u+1.  So the softmax runs under the MFMAs of the same wave.
+// row max of unit u+1 (D = 64) or has nothing to do (D = 128, see below).  So
+// the softmax runs under the MFMAs of the same wave.
+//
+// Running max, exact for any value it takes.  D = 64: the row max of the next
+// unit (taken under the PV MFMAs, where the VALU is otherwise idle) raises it
+// lazily, only by more than kTau.  D = 128: no max on the common path; a
+// unit's probabilities are taken against the running max as it stands, and
+// only when it is still -inf or some lane's sum over the unit exceeds 2^64 is
+// the unit's exact max folded in, the accumulators rescaled and the unit's
+// probabilities taken again (measured 2-3 % faster at D = 128; at D = 64 the
+// check after the exponentials sits on the critical path and costs more than
+// the max it saves).
 //
 // K and V tiles stream from HBM/L2 straight into LDS with buffer loads (two
 // K slots, two V slots).  At the top of iteration u one barrier frees the K
@@ -49,7 +60,12 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;     // lazy-rescale threshold of the running max, log2 units
+constexpr float kTau = 8.0f;     // lazy-rescale threshold of the running max, log2 units (D = 64)
+constexpr float kSumMax = 1.8446744e19f;   // 2^64: largest lane sum over a unit kept without rescale (D = 128)
+
+// Where the running max is kept current (see the file comment).
+template <int D>
+constexpr bool max_under_pv() { return D == 64; }
 
 // 16-byte chunk swizzles of a [key][D] bf16 tile whose rows are CPR chunks long.
 // K is read with ds_read_b128 down 16 consecutive rows; V with ds_read_b64_tr_b16
@@ -206,18 +222,29 @@ __device__ __forceinline__ void scores_only(const char* ks, const bf16x8 (&qf)[C
 // Probabilities j in [j0, j1) of the current unit: exp2 of the scaled,
 // max-shifted scores (in place), their running sum, and bf16 copies (pairs)
 // for the PV MFMAs.
+// With max_under_pv the scores are overwritten by their probabilities;
+// otherwise they are kept for a possible second pass (rescale_redo).
 template <int BS, int D, class C = Cfg<BS, D>>
 __device__ __forceinline__ void probs(floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float c2, float m_use,
                                       float& ls, int j0, int j1) {
+  float prev = 0.f;
 #pragma unroll
   for (int j = j0; j < j1; ++j) {
     const int t = j / 16, v2 = j % 16;
     const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][v2], c2, -m_use));
-    sc[t][v2] = p;
     ls += p;
-    if (j & 1) {
-      pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)sc[t][v2 - 1];
-      pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+    if constexpr (max_under_pv<D>()) {
+      sc[t][v2] = p;
+      if (j & 1) {
+        pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)sc[t][v2 - 1];
+        pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+      }
+    } else {
+      if (j & 1) {
+        pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)prev;
+        pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+      }
+      prev = p;
     }
   }
 }
@@ -255,7 +282,8 @@ __device__ __forceinline__ void phase_b(const char* ks, const bf16x8 (&qf)[C::DS
 }
 
 // Phase C: O^T += V^T P^T for the current unit, interleaved with the row max
-// of the next unit's scores when NEXT.  V operands are read AHEAD steps ahead.
+// of the next unit's scores when NEXT and max_under_pv.  V operands are read
+// AHEAD steps ahead.
 template <int BS, int D, bool NEXT, class C = Cfg<BS, D>>
 __device__ __forceinline__ void phase_c(const char* vs, const bf16x8 (&pb)[C::KC][2], floatx16 (&acc)[C::DT],
                                         const floatx16 (&sn)[C::KC], float& mx, int lane) {
@@ -272,7 +300,7 @@ __device__ __forceinline__ void phase_c(const char* vs, const bf16x8 (&pb)[C::KC
     if (s + AHEAD < NSTEP) vf[s + AHEAD] = read_v<BS, D>(vs, s + AHEAD, lane);
     const int dt = s % C::DT, h2 = (s / C::DT) & 1, t = s / (2 * C::DT);
     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], pb[t][h2], acc[dt], 0, 0, 0);
-    if constexpr (NEXT) {
+    if constexpr (NEXT && max_under_pv<D>()) {
 #pragma unroll
       for (int j = s * MPS; j < (s + 1) * MPS && j < NM; ++j) mx = fmaxf(mx, sn[j / 16][j % 16]);
     }
@@ -364,10 +392,19 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     voff[it] = dma_src_off<BS, D, true>(it, wave, lane);
   }
 
-  // Fold a unit's row max (raw score units, this lane's half) into the
-  // running max.  It is only raised when some lane's new max exceeds it by
-  // more than kTau (log2 units): p <= 2^kTau stays safe in bf16/fp32 and most
-  // updates skip the rescale of the output accumulators.  Exact for any m_run.
+  // This lane's max over a unit's (masked) scores, in raw score units.
+  auto unit_max = [&](const floatx16 (&sc)[C::KC]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < C::KC; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, sc[t][v2]);
+    return mx;
+  };
+  // D = 64: fold a unit's row max (raw score units, this lane's half) into
+  // the running max.  It is only raised when some lane's new max exceeds it
+  // by more than kTau (log2 units): p <= 2^kTau stays safe in bf16/fp32 and
+  // most updates skip the rescale of the output accumulators.
   auto fold_max = [&](float mx) __attribute__((always_inline)) {
     mx = xhalf_max(mx) * c2;
     if (__any(mx > m_run + kTau)) {
@@ -381,6 +418,24 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
       l_run *= alpha;
       ls_blk *= alpha;
     }
+  };
+  // D = 128: the unit's probabilities overflowed the safe range, or nothing
+  // is accumulated yet: fold in the unit's exact max, rescale what is
+  // accumulated (nothing when m_run was -inf), take the probabilities again.
+  auto rescale_redo = [&](floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float& ls) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_run, xhalf_max(unit_max(sc)) * c2);
+    if (m_new != m_run) {
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
+      l_run *= alpha;
+      ls_blk *= alpha;
+      m_run = m_new;
+    }
+    ls = 0.f;
+    probs<BS, D>(sc, pb, c2, m_run == -INFINITY ? 0.f : m_run, ls, 0, C::KC * 16);
   };
 
   floatx16 sa[C::KC], sb[C::KC];     // scores of the current and the next unit
@@ -398,16 +453,11 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     __syncthreads();
     scores_only<BS, D>(k0s, qf, sa, l32, hf);
     if (nv0 < C::SUB) mask_scores<BS, D>(sa, nv0, hf);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < C::KC; ++t)
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) mx = fmaxf(mx, sa[t][v2]);
-    fold_max(mx);
+    if constexpr (max_under_pv<D>()) fold_max(unit_max(sa));
   }
 
   // Iteration u: K[u+1] sits in slot (u+1)%2, V[u] in slot u%2.  sc holds
-  // unit u's scores (masked, max folded in); sn receives unit u+1's.  Inside
+  // unit u's scores (masked; max folded in at D = 64); sn receives unit u+1's.  Inside
   // the unrolled loop the next unit's scores are always computed (for the
   // last unit from a stale K slot, then discarded), which keeps one code path.
   auto iter = [&](auto next_tag, int u, floatx16 (&sc)[C::KC], floatx16 (&sn)[C::KC], const char* ks_next,
@@ -427,6 +477,9 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     bf16x8 pb[C::KC][2];
     float ls = 0.f;
     phase_b<BS, D, NEXT>(ks_next, qf, sc, sn, pb, c2, m_use, ls, l32, hf);
+    if constexpr (!max_under_pv<D>()) {
+      if (__any(m_run == -INFINITY || ls > kSumMax)) rescale_redo(sc, pb, ls);
+    }
     ls = xhalf_sum(ls);
     l_run += ls;
     ls_blk += ls;
@@ -441,7 +494,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
       if (has_next && nvn < C::SUB) mask_scores<BS, D>(sn, nvn, hf);
     }
     phase_c<BS, D, NEXT>(vs_cur, pb, acc, sn, mx, lane);
-    if constexpr (NEXT) fold_max(has_next ? mx : -INFINITY);   // a stale next unit adds nothing
+    if constexpr (NEXT && max_under_pv<D>()) fold_max(has_next ? mx : -INFINITY);   // a stale next unit adds nothing
   };
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;

@@ -104,6 +104,35 @@ def test_all_blocks_is_dense_attention(bsa, dtype):
                 assert abs(mg[e] - want) <= tol["mass"]
 
 
+@pytest.mark.parametrize("D,bs", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("jump", [100.0, 180.0])
+def test_forward_running_max_jumps(bsa, D, bs, jump):
+    """Scores that jump by `jump` log2 units from one key block to the next
+    (very negative, moderate, very positive, moderate), so the running max
+    must be raised far beyond any lazy threshold, and beyond the range where
+    2^x stays finite in fp32 (180).  Checked against the oracle like any
+    forward (O, LSE, block mass)."""
+    rng = np.random.default_rng(int(jump) + D + bs)
+    B, H, N = 1, 2, 4 * bs
+    c2 = default_scale(D) * np.log2(np.e)
+    a = float(np.ceil(jump / (2.0 * D * c2)))           # q = 2, k = +-a: scores 2aD * scale
+    q = np.full((B, H, N, D), 2.0, np.float32) + 0.05 * rng.normal(size=(B, H, N, D)).astype(np.float32)
+    k = 0.5 * rng.normal(size=(B, H, N, D)).astype(np.float32)
+    k[:, :, 0:bs] -= a
+    k[:, :, 2 * bs:3 * bs] += a
+    v = rng.normal(size=(B, H, N, D)).astype(np.float32)
+    q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    nb = 4
+    rp, ci = O.rows_to_csr([np.arange(nb)] * (B * H * nb))
+    mask = bsa.csr_from_host(rp, ci, "cuda")
+    qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
+    o, lse, mass = bsa.bsa_forward(qd, kd, vd, mask, bs)
+    torch.cuda.synchronize()
+    err = compare_forward(q, k, v, bs, rp, ci, default_scale(D), list(range(B * H * nb)), to_host(o),
+                          to_host(lse), to_host(mass), "bf16")
+    assert_forward_within(err, "bf16", f"jump={jump} D={D} bs={bs}")
+
+
 def test_invalid_ids_and_entries_past_capacity_are_ignored(bsa):
     rng = np.random.default_rng(2)
     B, H, N, D, bs = 1, 1, 500, 64, 128
