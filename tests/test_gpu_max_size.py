@@ -1,0 +1,77 @@
+"""GPU parity at the largest shape the ABI accepts for D = 128, block 128:
+4096 key blocks per row, a ragged last block and B*H*N*D just under 2^31
+elements per tensor (4.2 GB of bf16 each).  Inputs are seeded device
+normals with a shared component per 4 blocks.  The oracle checks the
+estimator's mask on the last head and the forward on sampled rows of the
+first and last heads, whose Q/K/V are copied to the host."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import bsa_oracle as O
+from tests.gpu_helpers import (assert_forward_within, compare_forward, compare_masks, default_scale, f32,
+                               sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+B, H, D, BS = 1, 31, 128, 128
+N = 4096 * BS - 77                      # 4096 blocks, the last one ragged
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_16_amd as m
+    m.load()
+    return m
+
+
+def _inputs(gen):
+    """Q = 0.3 e_Q + U, K = e_K + U, V = e_V with e ~ N(0, 1) and U one N(0, 1)
+    row per 512 tokens (4 blocks): a query block's pooled score is high on the
+    4 blocks sharing its U.  Most rows keep those 4 (plus the forced prefix
+    blocks); rows whose U is weak spread their mass and keep up to ~2000, so
+    row lengths range widely (about 50 on average)."""
+    q, k, v = (torch.empty((B, H, N, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    for h in range(H):                  # one head at a time keeps the fp32 temporaries small
+        u = torch.randn((-(-N // 512), D), generator=gen, device="cuda").repeat_interleave(512, dim=0)[:N]
+        q[0, h] = (0.3 * torch.randn((N, D), generator=gen, device="cuda") + u).to(torch.bfloat16)
+        k[0, h] = (torch.randn((N, D), generator=gen, device="cuda") + u).to(torch.bfloat16)
+        v[0, h] = torch.randn((N, D), generator=gen, device="cuda").to(torch.bfloat16)
+    return q, k, v
+
+
+def _head(x, h):
+    return x[0, h].float().cpu().numpy()[None, None]
+
+
+def test_estimate_and_forward_at_max_size(bsa):
+    assert B * H * N * D < 2 ** 31 and B * H * N * D > 0.96 * 2 ** 31
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260)
+    q, k, v = _inputs(gen)
+    p = f32(0.9)
+    mask = bsa.bsa_estimate_mask(q, k, p, BS, keep_prefix_tokens=200)
+    o, lse, mass = bsa.bsa_forward(q, k, v, mask, BS)
+    torch.cuda.synchronize()
+    rp, ci = mask.to_host()
+    nb = O.num_blocks(N, BS)
+    assert nb == 4096 and rp.size == B * H * nb + 1 and rp[-1] == ci.size
+    scale = default_scale(D)
+    for h in (0, H - 1):
+        qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
+        # the head's rows as a one-head CSR
+        a, z = int(rp[h * nb]), int(rp[(h + 1) * nb])
+        rph, cih = rp[h * nb:(h + 1) * nb + 1] - a, ci[a:z]
+        if h == H - 1:
+            _, _, sels = O.estimate_mask(qh, kh, BS, p, scale, keep_prefix_tokens=200)
+            rows, bad, band = compare_masks(rph, cih, sels, 1, nb, p)
+            assert not bad, f"head {h}: {len(bad)} of {rows} rows differ outside the band"
+        sel = sample_rows(nb, nb, 6, seed=h)
+        oh = o[0, h].float().cpu().numpy()[None, None].astype(np.float64)
+        lh = lse[0, h].cpu().numpy()[None, None].astype(np.float64)
+        mh = mass[a:z].cpu().numpy().astype(np.float64)
+        err = compare_forward(qh, kh, vh, BS, rph, cih, scale, sel, oh, lh, mh, "bf16")
+        assert_forward_within(err, "bf16", f"max size, head {h}")
