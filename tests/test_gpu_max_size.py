@@ -28,17 +28,17 @@ def bsa():
     return m
 
 
-def _inputs(gen):
-    """Q = 0.3 e_Q + U, K = e_K + U, V = e_V with e ~ N(0, 1) and U one N(0, 1)
-    row per 512 tokens (4 blocks): a query block's pooled score is high on the
-    4 blocks sharing its U.  Most rows keep those 4 (plus the forced prefix
+def _inputs(gen, su=1.0, sk=1.0):
+    """Q = 0.3 e_Q + U, K = sk e_K + U, V = e_V with e ~ N(0, 1) and U one
+    su N(0, 1) row per 512 tokens (4 blocks): a query block's pooled score is
+    high on the 4 blocks sharing its U.  Most rows keep those 4 (plus the forced prefix
     blocks); rows whose U is weak spread their mass and keep up to ~2000, so
     row lengths range widely (about 50 on average)."""
     q, k, v = (torch.empty((B, H, N, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
     for h in range(H):                  # one head at a time keeps the fp32 temporaries small
-        u = torch.randn((-(-N // 512), D), generator=gen, device="cuda").repeat_interleave(512, dim=0)[:N]
+        u = su * torch.randn((-(-N // 512), D), generator=gen, device="cuda").repeat_interleave(512, dim=0)[:N]
         q[0, h] = (0.3 * torch.randn((N, D), generator=gen, device="cuda") + u).to(torch.bfloat16)
-        k[0, h] = (torch.randn((N, D), generator=gen, device="cuda") + u).to(torch.bfloat16)
+        k[0, h] = (sk * torch.randn((N, D), generator=gen, device="cuda") + u).to(torch.bfloat16)
         v[0, h] = torch.randn((N, D), generator=gen, device="cuda").to(torch.bfloat16)
     return q, k, v
 
@@ -75,3 +75,41 @@ def test_estimate_and_forward_at_max_size(bsa):
         mh = mass[a:z].cpu().numpy().astype(np.float64)
         err = compare_forward(qh, kh, vh, BS, rph, cih, scale, sel, oh, lh, mh, "bf16")
         assert_forward_within(err, "bf16", f"max size, head {h}")
+
+
+def test_backward_at_max_size(bsa):
+    """dQ, dK, dV at the same shape over a sparse host-built mask (the
+    diagonal block plus 0-5 random blocks per row, the ragged last key block
+    in several rows), against the oracle on the last head.  Q and K at the
+    training workload's scale (entries of std ~0.6): the 2e-2 bar on the
+    gradients is absolute, and the bf16 rounding of P and dS inside the MFMAs
+    grows with |Q| and |K|."""
+    from tests.gpu_helpers import compare_backward
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261)
+    q, k, v = _inputs(gen, su=0.5, sk=0.5)
+    g = torch.empty_like(q)
+    for h in range(H):
+        g[0, h] = torch.randn((N, D), generator=gen, device="cuda").to(torch.bfloat16)
+    nb = O.num_blocks(N, BS)
+    rng = np.random.default_rng(5)
+    rows = []
+    for r in range(B * H * nb):
+        i = r % nb
+        extra = rng.choice(nb, size=int(rng.integers(0, 6)), replace=False)
+        if r % 97 == 0:
+            extra = np.append(extra, nb - 1)
+        rows.append(np.unique(np.append(extra, i)))
+    rp, ci = O.rows_to_csr(rows)
+    mask = bsa.csr_from_host(rp, ci, "cuda")
+    o, lse, _ = bsa.bsa_forward(q, k, v, mask, BS, want_mass=False)
+    dq, dk, dv = bsa.bsa_backward(q, k, v, o, g, lse, mask, BS)
+    torch.cuda.synchronize()
+    h = H - 1
+    x = {"q": _head(q, h), "k": _head(k, h), "v": _head(v, h), "g": _head(g, h)}
+    a, z = int(rp[h * nb]), int(rp[(h + 1) * nb])
+    rph, cih = rp[h * nb:(h + 1) * nb + 1] - a, ci[a:z]
+    grads = {n: t[0, h].float().cpu().numpy()[None, None].astype(np.float64)
+             for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    err = compare_backward(x, BS, rph, cih, default_scale(D), [(0, 0)], grads, "bf16")
+    assert err["excess"] <= 0.0, f"gradient errors at max size {err}"
