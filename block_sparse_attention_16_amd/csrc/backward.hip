@@ -203,36 +203,52 @@ __global__ __launch_bounds__(256) void delta_kernel(const TO* __restrict__ o, co
 
 // ---------------------------------------------------------------------------
 // CSC transpose: column (bh, j) lists the query blocks i whose row holds j,
-// ascending; csc_start/csc_count index csc_row.
+// ascending; csc_start/csc_count index csc_row.  One workgroup of 1024
+// threads per head.  The head's rows split into T contiguous chunks, one per
+// wavefront (T = 16, fewer when nb > 1024, so the per-chunk column counts fit
+// in LDS).  Each wavefront counts its chunk's entries per column.  One scan
+// over (column, chunk) gives every chunk its cursor into each column.  Each
+// wavefront then writes its rows in order, so every column lists its rows
+// ascending without a barrier per row.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ row_ptr,
-                                                  const int32_t* __restrict__ col_idx, int64_t cap, int nb,
-                                                  int32_t* __restrict__ csc_start, int32_t* __restrict__ csc_count,
-                                                  int32_t* __restrict__ csc_row) {
-  __shared__ int cnt[4096];
-  __shared__ int cur[4096];
-  __shared__ int wsum[4];
-  const int bh = blockIdx.x, tid = threadIdx.x;
+constexpr int kCscThreads = 1024;
+constexpr int kCscLds = 16384;            // ints of per-chunk column counters
+
+__global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx, int64_t cap, int nb,
+                                                          int32_t* __restrict__ csc_start,
+                                                          int32_t* __restrict__ csc_count,
+                                                          int32_t* __restrict__ csc_row) {
+  __shared__ int cnt[kCscLds];            // [T][nb]: counts, then cursors
+  __shared__ int64_t rp[4097];            // the head's clamped row offsets
+  __shared__ int wsum[kCscThreads / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int T = min(kCscThreads / 64, kCscLds / nb);     // row chunks (>= 4 for nb <= 4096)
+  const int rows_per = (nb + T - 1) / T;
   auto clampe = [&](int64_t e) { return e < 0 ? (int64_t)0 : (e > cap ? cap : e); };
-  const int64_t hb = clampe(row_ptr[(size_t)bh * nb]), he = clampe(row_ptr[(size_t)bh * nb + nb]);
-  for (int j = tid; j < nb; j += 256) cnt[j] = 0;
+  for (int i = tid; i <= nb; i += kCscThreads) rp[i] = clampe(row_ptr[(size_t)bh * nb + i]);
+  for (int x = tid; x < T * nb; x += kCscThreads) cnt[x] = 0;
   __syncthreads();
-  for (int64_t e = hb + tid; e < he; e += 256) {
-    const int j = col_idx[e];
-    if (j >= 0 && j < nb) atomicAdd(&cnt[j], 1);
+  const int64_t hb = rp[0], he = rp[nb];
+  const int r0 = w * rows_per, r1 = min(nb, r0 + rows_per);
+  if (w < T) {
+    int* mine = cnt + w * nb;
+    for (int i = r0; i < r1; ++i) {
+      const int64_t a = max(rp[i], hb), b = min(rp[i + 1], he);
+      for (int64_t e = a + lane; e < b; e += 64) {
+        const int j = col_idx[e];
+        if (j >= 0 && j < nb) atomicAdd(&mine[j], 1);
+      }
+    }
   }
   __syncthreads();
-  // exclusive scan of cnt over nb entries: per-thread chunks, then thread totals
-  const int chunk = (nb + 255) / 256;
+  // column totals and their exclusive scan; each thread owns consecutive columns
+  const int chunk = (nb + kCscThreads - 1) / kCscThreads;
   const int c0 = tid * chunk;
   int run = 0;
-  for (int j = c0; j < c0 + chunk && j < nb; ++j) {
-    const int v = cnt[j];
-    cur[j] = run;
-    run += v;
-  }
+  for (int j = c0; j < c0 + chunk && j < nb; ++j)
+    for (int c = 0; c < T; ++c) run += cnt[c * nb + j];
   int x = run;
-  const int lane = tid & 63, w = tid >> 6;
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
@@ -242,23 +258,30 @@ __global__ __launch_bounds__(256) void csc_kernel(const int32_t* __restrict__ ro
   int base = (int)hb + x - run;
   for (int ww = 0; ww < w; ++ww) base += wsum[ww];
   for (int j = c0; j < c0 + chunk && j < nb; ++j) {
-    cur[j] += base;
-    csc_start[(size_t)bh * nb + j] = cur[j];
-    csc_count[(size_t)bh * nb + j] = cnt[j];
+    int pos = base;
+    for (int c = 0; c < T; ++c) {          // chunk c's cursor into column j
+      const int v = cnt[c * nb + j];
+      cnt[c * nb + j] = pos;
+      pos += v;
+    }
+    csc_start[(size_t)bh * nb + j] = base;
+    csc_count[(size_t)bh * nb + j] = pos - base;
+    base = pos;
   }
   __syncthreads();
-  // fill, one row at a time so each column comes out ascending
-  for (int i = 0; i < nb; ++i) {
-    const int64_t a = clampe(row_ptr[(size_t)bh * nb + i]), b = clampe(row_ptr[(size_t)bh * nb + i + 1]);
-    for (int64_t e = a + tid; e < b; e += 256) {
-      const int j = col_idx[e];
-      if (j >= 0 && j < nb) {
-        const int pos = cur[j];
-        cur[j] = pos + 1;
-        if (pos >= hb && pos < he) csc_row[pos] = i;
+  // fill: each wavefront writes its rows in ascending order
+  if (w < T) {
+    int* cur = cnt + w * nb;
+    for (int i = r0; i < r1; ++i) {
+      const int64_t a = max(rp[i], hb), b = min(rp[i + 1], he);
+      for (int64_t e = a + lane; e < b; e += 64) {
+        const int j = col_idx[e];
+        if (j >= 0 && j < nb) {
+          const int pos = atomicAdd(&cur[j], 1);       // distinct slots even for a repeated id
+          if (pos >= hb && pos < he) csc_row[pos] = i;
+        }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -729,7 +752,7 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   if (!bf) launch_delta<float, float>(p, o, d_o, lse, 1, w, s);
   else if (delta_given) launch_delta<float, __bf16>(p, o32, d_o, lse, 1, w, s);
   else launch_delta<__bf16, __bf16>(p, o, d_o, lse, 0, w, s);
-  csc_kernel<<<p.B * p.H, 256, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start,
+  csc_kernel<<<p.B * p.H, kCscThreads, 0, s>>>(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, w.csc_start,
                                       w.csc_count, w.csc_row);
   if (!bf) return launch_backward_fp32(p, q, k, v, d_o, scale, mask, dq, dk, dv, w, s);
   if (p.bs == 128 && p.D == 128)
