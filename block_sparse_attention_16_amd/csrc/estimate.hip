@@ -664,7 +664,8 @@ __device__ __forceinline__ int spot_intervals(const BlockGeo& g, int prefix, int
 }
 
 // One wavefront per mask row: the row's key blocks under its head's pattern
-// -> selection bitmask and count.  Unknown kinds give dense rows.
+// -> selection bitmask and count, one block per lane and one ballot (two
+// bitmask words) per 64 blocks.  Unknown kinds give dense rows.
 __global__ __launch_bounds__(kThreads) void pattern_kernel(const int32_t* __restrict__ head_kind, int nb, int R,
                                                            int N, int bs, int prefix, int F, int band, int period,
                                                            const int32_t* __restrict__ stripes, int n_stripes,
@@ -689,47 +690,41 @@ __global__ __launch_bounds__(kThreads) void pattern_kernel(const int32_t* __rest
   if (kind == BSA_PATTERN_TEMPORAL && vi) ni = spot_intervals(gi, prefix, F, ai, bi);
   const int fi0 = vi ? (gi.vlo - prefix) / F : 0, fi1 = vi ? (gi.hi - 1 - prefix) / F : -1;
   int cnt = 0;
-  for (int w0 = 0; w0 < words; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t word = 0u;
-    if (w < words) {
-      for (int b = 0; b < 32; ++b) {
-        const int j = w * 32 + b;
-        if (j >= nb) break;
-        const BlockGeo gj = block_geo(j, bs, N, prefix);
-        const bool vj = gj.vlo < gj.hi;
-        const int d = i - j;
-        bool keep;
-        if (gi.text || gj.text) {
-          keep = true;
-        } else if (kind == BSA_PATTERN_SPATIAL) {
-          const int fj0 = (gj.vlo - prefix) / F, fj1 = (gj.hi - 1 - prefix) / F;
-          keep = vi && vj && fi0 <= fj1 && fj0 <= fi1;
-        } else if (kind == BSA_PATTERN_TEMPORAL) {
-          keep = false;
-          if (vi && vj) {
-            int aj[2], bj[2];
-            const int nj = spot_intervals(gj, prefix, F, aj, bj);
-            for (int x = 0; x < ni; ++x)
-              for (int y = 0; y < nj; ++y) keep = keep || (ai[x] <= bj[y] && aj[y] <= bi[x]);
-          }
-        } else if (kind == BSA_PATTERN_DIAGONAL) {
-          keep = abs(d) <= band;
-        } else if (kind == BSA_PATTERN_MULTI_DIAGONAL) {
-          const int m = ((d % period) + period) % period;
-          keep = min(m, period - m) <= band;
-        } else if (kind == BSA_PATTERN_STRIPES) {
-          keep = ((stripe_bits[j >> 5] >> (j & 31)) & 1u) || abs(d) <= band;
-        } else {
-          keep = true;                       // BSA_PATTERN_DENSE and unknown kinds
+  for (int j0 = 0; j0 < nb; j0 += 64) {      // lane l decides block j0 + l; one ballot per 64 blocks
+    const int j = j0 + lane;
+    bool keep = false;
+    if (j < nb) {
+      const BlockGeo gj = block_geo(j, bs, N, prefix);
+      const bool vj = gj.vlo < gj.hi;
+      const int d = i - j;
+      if (gi.text || gj.text) {
+        keep = true;
+      } else if (kind == BSA_PATTERN_SPATIAL) {
+        const int fj0 = (gj.vlo - prefix) / F, fj1 = (gj.hi - 1 - prefix) / F;
+        keep = vi && vj && fi0 <= fj1 && fj0 <= fi1;
+      } else if (kind == BSA_PATTERN_TEMPORAL) {
+        if (vi && vj) {
+          int aj[2], bj[2];
+          const int nj = spot_intervals(gj, prefix, F, aj, bj);
+          for (int x = 0; x < ni; ++x)
+            for (int y = 0; y < nj; ++y) keep = keep || (ai[x] <= bj[y] && aj[y] <= bi[x]);
         }
-        if (keep) word |= 1u << b;
+      } else if (kind == BSA_PATTERN_DIAGONAL) {
+        keep = abs(d) <= band;
+      } else if (kind == BSA_PATTERN_MULTI_DIAGONAL) {
+        const int m = ((d % period) + period) % period;
+        keep = min(m, period - m) <= band;
+      } else if (kind == BSA_PATTERN_STRIPES) {
+        keep = ((stripe_bits[j >> 5] >> (j & 31)) & 1u) || abs(d) <= band;
+      } else {
+        keep = true;                         // BSA_PATTERN_DENSE and unknown kinds
       }
-      bits[(size_t)r * words + w] = word;
     }
-    cnt += __popc(word);
+    const uint64_t sel = __ballot(keep);
+    const int w = j0 / 32 + (lane & 1);      // bitmask words 2c and 2c + 1
+    if (lane < 2 && w < words) bits[(size_t)r * words + w] = (uint32_t)(sel >> (32 * (lane & 1)));
+    cnt += __popcll(sel);
   }
-  cnt = wave_sum_i(cnt);
   if (lane == 0) counts[r] = cnt;
 }
 
