@@ -16,7 +16,8 @@
 //                   Abstract)
 //   select_full_kernel  (every block a candidate) one wavefront per row:
 //                   softmax over the row, Top-p cut found by bisection on the
-//                   ordered logit bits (no sort), ties at the cut broken by
+//                   ordered logit bits (no sort; it stops once a single block
+//                   is left in the cut's range), ties at the cut broken by
 //                   lower block id, forced prefix blocks; the selection of
 //                   64 blocks is one ballot -> selection bitmask
 //   select_kernel   the same rule over each row's candidate blocks (reduced
@@ -33,8 +34,8 @@
 // Structured head masks (SVG page, Abstract: spatial and temporal heads;
 // Sparse-vDiT page, Abstract: diagonal, multi-diagonal and vertical-stripe
 // patterns): pattern_kernel evaluates the block relation of each row's head
-// with interval arithmetic on frames and spatial positions, into the same
-// bitmask, then the same csr_kernel.
+// with interval arithmetic on frames and spatial positions, one key block per
+// lane, into the same bitmask, then the same csr_kernel.
 #include "bsa_internal.h"
 
 namespace bsa {
