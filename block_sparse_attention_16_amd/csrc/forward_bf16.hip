@@ -323,7 +323,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
-  __shared__ float lse2_s[BS];
+  __shared__ __attribute__((aligned(16))) float lse2_s[BS];
 
   // blockIdx -> mask row, dealt to the 8 XCDs round-robin by the dispatcher
   // (finer-grained than any contiguous split, which balances rows of unequal
@@ -538,15 +538,52 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   __syncthreads();
 
   // ---- exact block mass: mean over valid queries of exp2(part - lse2) ----
-  for (int it = wave; it < n_e; it += C::NW) {
-    const int64_t e = e_begin + it;
-    const int j_raw = col_idx[e];
-    float s = 0.f;
-    if (j_raw >= 0 && j_raw < nb) {
-      for (int t = lane; t < nq; t += 64) s += __builtin_amdgcn_exp2f(part[e * BS + t] - lse2_s[t]);
+  if constexpr (D == 128) {
+    // Four entries per wavefront at a time, 16 lanes each: lane c of a group
+    // sums queries [QPL c, QPL c + QPL) (16-byte loads of part and lse2),
+    // then four xor-shuffles within the group.  (At D = 64 this form made
+    // the whole kernel ~4 % slower, with the main loop unchanged; D = 64
+    // keeps one entry per wavefront.)
+    constexpr int QPL = BS / 16;               // queries per lane
+    const int grp = lane >> 4, c = lane & 15;
+    float l2[QPL];
+#pragma unroll
+    for (int x = 0; x < QPL; x += 4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(lse2_s + QPL * c + x);
+      l2[x] = v4.x; l2[x + 1] = v4.y; l2[x + 2] = v4.z; l2[x + 3] = v4.w;
     }
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) mass[e] = s / (float)nq;
+    for (int base = wave * 4; base < n_e; base += C::NW * 4) {
+      const int it = base + grp;
+      const bool live = it < n_e;
+      const int64_t e = e_begin + (live ? it : 0);
+      const int j_raw = live ? col_idx[e] : -1;
+      float s = 0.f;
+      if (j_raw >= 0 && j_raw < nb) {
+        const float* pe = part + e * BS + QPL * c;
+#pragma unroll
+        for (int x = 0; x < QPL; x += 4) {
+          const float4 p4 = *reinterpret_cast<const float4*>(pe + x);
+          const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+            if (QPL * c + x + y < nq) s += __builtin_amdgcn_exp2f(pv[y] - l2[x + y]);
+        }
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (live && c == 0) mass[e] = s / (float)nq;
+    }
+  } else {
+    for (int it = wave; it < n_e; it += C::NW) {
+      const int64_t e = e_begin + it;
+      const int j_raw = col_idx[e];
+      float s = 0.f;
+      if (j_raw >= 0 && j_raw < nb) {
+        for (int t = lane; t < nq; t += 64) s += __builtin_amdgcn_exp2f(part[e * BS + t] - lse2_s[t]);
+      }
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) mass[e] = s / (float)nq;
+    }
   }
 }
 
