@@ -538,12 +538,12 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   __syncthreads();
 
   // ---- exact block mass: mean over valid queries of exp2(part - lse2) ----
-  if constexpr (D == 128) {
+  if constexpr (D == 128 && BS == 128) {
     // Four entries per wavefront at a time, 16 lanes each: lane c of a group
     // sums queries [QPL c, QPL c + QPL) (16-byte loads of part and lse2),
-    // then four xor-shuffles within the group.  (At D = 64 this form made
-    // the whole kernel ~4 % slower, with the main loop unchanged; D = 64
-    // keeps one entry per wavefront.)
+    // then four xor-shuffles within the group.  (Measured slower elsewhere:
+    // ~4 % for the whole kernel at D = 64 with the main loop unchanged, 1 %
+    // with 64-token blocks; those keep one entry per wavefront.)
     constexpr int QPL = BS / 16;               // queries per lane
     const int grp = lane >> 4, c = lane & 15;
     float l2[QPL];
