@@ -691,9 +691,10 @@ template <int BS, int D>
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
                            float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, bool delta_given,
                            const BackwardWs& w, hipStream_t s) {
-  const int T = tail_rows(p.R), t0 = p.R - T;
-  launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, T, w.order_q, s);
-  launch_tail_order(nullptr, 0, w.csc_count, t0, T, w.order_k, s);
+  const int Tq = query_tail_rows(p.R, BS), t0 = p.R - Tq;   // dQ grid: rows
+  const int Tk = tail_rows(p.R), t0k = p.R - Tk;              // dK/dV grid: columns
+  launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, Tq, w.order_q, s);
+  launch_tail_order(nullptr, 0, w.csc_count, t0k, Tk, w.order_k, s);
   dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
@@ -702,7 +703,7 @@ hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const
   dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
-      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale, w.order_k, t0);
+      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), p.N, p.nb, scale, w.order_k, t0k);
   return hipGetLastError();
 }
 

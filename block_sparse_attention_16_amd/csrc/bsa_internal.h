@@ -72,11 +72,12 @@ hipError_t launch_permute_rows(int64_t heads, int n, int row_bytes, const void* 
 // forward workgroups).
 constexpr int kTailRows = 2048;
 inline int tail_rows(int R) { return R < kTailRows ? R : kTailRows; }
-// The forward's tail with 64-token blocks (two-wave workgroups): 1024 rows
-// measured 3 % faster than 2048 on the training workload (3072 and 4096
-// slower); with 128-token blocks 2048 stays best.  At most tail_rows(R), the
-// size of the order array in the forward workspace.
-inline int fwd_tail_rows(int R, int bs) { return bs == 64 ? (R < 1024 ? R : 1024) : tail_rows(R); }
+// Tail of a grid with one workgroup per query block (forward, dQ).  With
+// 64-token blocks (two-wave workgroups) 1024 rows measured best on the
+// training workload: forward 3 % faster than with 2048 (3072 and 4096
+// slower), dQ ~1 % (the dK/dV grid keeps 2048).  With 128-token blocks 2048
+// stays best.  At most tail_rows(R), the size of the order arrays.
+inline int query_tail_rows(int R, int bs) { return bs == 64 ? (R < 1024 ? R : 1024) : tail_rows(R); }
 // Lengths are counts[r] when counts is non-null, else the CSR extents of
 // row_ptr clamped to [0, cap].
 void launch_tail_order(const int32_t* row_ptr, int64_t cap, const int32_t* counts, int r0, int T, int32_t* order,

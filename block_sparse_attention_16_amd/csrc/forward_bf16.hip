@@ -592,7 +592,7 @@ hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const voi
                        const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
                        hipStream_t s) {
   using C = Cfg<BS, D>;
-  const int T = fwd_tail_rows(p.R, BS), t0 = p.R - T;
+  const int T = query_tail_rows(p.R, BS), t0 = p.R - T;
   launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, T, w.order, s);
   if (o32 != nullptr)
     fwd_kernel<BS, D, true><<<p.R, C::THREADS, 0, s>>>(
