@@ -22,9 +22,9 @@
 //                   64 blocks is one ballot -> selection bitmask
 //   select_kernel   the same rule over each row's candidate blocks (reduced
 //                   search) -> selection bitmask
-//   csr_kernel      per workgroup of 32 rows: sum of the earlier rows' counts,
+//   csr_kernel      per workgroup of 8 rows: sum of the earlier rows' counts,
 //                   scan of its own -> CSR row_ptr; bitmasks -> ascending
-//                   col_idx (one wavefront per 8 rows, 64 blocks per store)
+//                   col_idx (one wavefront per 2 rows, 64 blocks per store)
 //
 // Mask narrowing (GSRS page, Abstract and Figure 4 caption: exact attention
 // weights, later searches restricted to an earlier step's blocks) reuses
@@ -546,15 +546,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   if (lane == 0) counts[r] = cnt;
 }
 
-// CSR assembly in one launch.  Workgroup b takes rows [32b, 32b + 32): it sums
+// CSR assembly in one launch.  Workgroup b takes rows [8b, 8b + 8): it sums
 // the counts of every earlier row (16-byte loads, wave and workgroup sums;
-// at most R counts, read from L2), scans its own 32 counts across lanes and
-// writes their row_ptr (and row_ptr[R]).  Then each wavefront writes 8 rows'
+// at most R counts, read from L2), scans its own 8 counts across lanes and
+// writes their row_ptr (and row_ptr[R]).  Then each wavefront writes 2 rows'
 // ids: for every 64 blocks of a row's bitmask (two words, uniform), lane l
 // stores block 64c + l at the row offset plus the number of set bits below
 // its own (mbcnt), so a row takes one masked store per 64 blocks.  Ids at
 // positions >= cap are dropped; row_ptr keeps the exact offsets.
-constexpr int kCsrRowsPerWave = 8;
+constexpr int kCsrRowsPerWave = 2;   // 2 of 2 / 4 / 8 measured best (more workgroups)
 constexpr int kCsrRows = 4 * kCsrRowsPerWave;     // rows per workgroup (<= 64)
 
 // Blocks j0 .. j0 + 63 of one row, selected by the 64-bit mask (hi:lo),
