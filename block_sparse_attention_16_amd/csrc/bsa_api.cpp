@@ -38,7 +38,7 @@ bsa_status make_problem(const bsa_shape* s, bsa::Problem* p) {
   if (s->block != 64 && s->block != 128)
     return fail(BSA_ERR_UNSUPPORTED, "block=%d: only 64 and 128 are built", s->block);
   if (s->dtype != BSA_BF16 && s->dtype != BSA_FP32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", s->dtype);
-  const int64_t nb = (s->N + s->block - 1) / s->block;
+  const int64_t nb = ((int64_t)s->N + s->block - 1) / s->block;
   if (nb > 4096) return fail(BSA_ERR_UNSUPPORTED, "%lld blocks per sequence exceed 4096", (long long)nb);
   const int64_t elems = (int64_t)s->B * s->H * s->N * s->D;
   if (elems >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "B*H*N*D must be below 2^31");

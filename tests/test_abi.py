@@ -88,6 +88,8 @@ def test_estimate_validation():
     assert _est(L, _shape(dtype=5)) == _lib.BSA_ERR_UNSUPPORTED
     assert _est(L, _shape(N=0)) == _lib.BSA_ERR_INVALID_ARG
     assert _est(L, _shape(N=64 * 4097)) == _lib.BSA_ERR_UNSUPPORTED   # more than 4096 blocks
+    assert _est(L, _shape(N=2 ** 31 - 1, block=128)) == _lib.BSA_ERR_UNSUPPORTED   # N + block - 1 past int32
+    assert b"blocks per sequence" in L.bsa_last_error()
     out = _csr()
     assert _est(L, s, cand=out, out=out) == _lib.BSA_ERR_INVALID_ARG   # candidate aliases out
     bad = _lib.BsaCsr(FAKE, None, 10)
