@@ -70,7 +70,7 @@ def _shape_of(q: torch.Tensor, block: int) -> BsaShape:
     return make_shape(B, H, N, D, block, _dtype_code(q))
 
 
-def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None, dtype=None):
+def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None, dtype=None, shape=None, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
@@ -79,6 +79,19 @@ def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None, dtype=N
         raise ValueError(f"{name} must match q in shape, dtype and device")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on q's device")
+
+
+def _check_csr(m: Csr, rows: int, name: str, device) -> None:
+    """The library reads row_ptr[0..rows] and at most capacity col_idx entries."""
+    for t, part in ((m.row_ptr, "row_ptr"), (m.col_idx, "col_idx")):
+        if t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+            raise ValueError(f"{name}.{part} must be a contiguous int32 tensor on q's device")
+    if m.row_ptr.numel() < rows + 1:
+        raise ValueError(f"{name}.row_ptr must hold B*H*nb + 1 = {rows + 1} entries")
 
 
 def _stream() -> int:
@@ -94,10 +107,18 @@ def bsa_workspace_size(shape: BsaShape, kind: int, capacity: int = 0) -> int:
 
 
 def _workspace(shape: BsaShape, kind: int, capacity: int, ws: torch.Tensor | None, device) -> torch.Tensor:
-    need = bsa_workspace_size(shape, kind, capacity)
+    """The caller's workspace, or a new one of the size the library asks for.
+    The library itself checks that it is large enough (sizes in bytes)."""
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        need = bsa_workspace_size(shape, kind, capacity)
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     return ws
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def num_rows(q: torch.Tensor, block: int) -> int:
@@ -122,19 +143,22 @@ def bsa_estimate_mask(q: torch.Tensor, k: torch.Tensor, top_p: float, block: int
         cap = R * nb if capacity is None else capacity
         out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
                   torch.empty(cap, dtype=torch.int32, device=q.device))
+    _check_csr(out, R, "out", q.device)
+    if candidate is not None:
+        _check_csr(candidate, R, "candidate", q.device)
     cand = ctypes.byref(candidate.c()) if candidate is not None else None
     oc = out.c()
     if sub_blocks == 1:
         ws = _workspace(shape, BSA_WS_ESTIMATE, 0, workspace, q.device)
         st = load().bsa_estimate_mask(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p), float(scale),
-                                      cand, int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(),
+                                      cand, int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), _nbytes(ws),
                                       _stream())
         check(st, "bsa_estimate_mask")
     else:
         ws = _workspace(shape, BSA_WS_ESTIMATE_HIER, 0, workspace, q.device)
         st = load().bsa_estimate_mask_hierarchical(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), float(top_p),
                                                    float(scale), cand, int(keep_prefix_tokens), int(sub_blocks),
-                                                   ctypes.byref(oc), ws.data_ptr(), ws.numel(), _stream())
+                                                   ctypes.byref(oc), ws.data_ptr(), _nbytes(ws), _stream())
         check(st, "bsa_estimate_mask_hierarchical")
     return out
 
@@ -145,7 +169,7 @@ def bsa_select_from_mass(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: 
     """Mask narrowing: Top-p over the block masses aligned with ``mask`` -> CSR
     (see bsa_select_from_mass in include/bsa.h).  ``q`` supplies the shape only."""
     _check(q, "q")
-    _check(mass, "mass", dtype=torch.float32)
+    _check(mass, "mass", dtype=torch.float32, device=q.device)
     if mass.numel() < mask.capacity:
         raise ValueError("mass must hold mask.capacity entries")
     shape = _shape_of(q, block)
@@ -154,10 +178,12 @@ def bsa_select_from_mass(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: 
     if out is None:
         out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
                   torch.empty(R * nb, dtype=torch.int32, device=q.device))
+    _check_csr(mask, R, "mask", q.device)
+    _check_csr(out, R, "out", q.device)
     ws = _workspace(shape, BSA_WS_SELECT_FROM_MASS, 0, workspace, q.device)
     mc, oc = mask.c(), out.c()
     st = load().bsa_select_from_mass(ctypes.byref(shape), ctypes.byref(mc), mass.data_ptr(), float(top_p),
-                                     int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), ws.numel(),
+                                     int(keep_prefix_tokens), ctypes.byref(oc), ws.data_ptr(), _nbytes(ws),
                                      _stream())
     check(st, "bsa_select_from_mass")
     return out
@@ -183,13 +209,14 @@ def bsa_structured_mask(q: torch.Tensor, head_kind: torch.Tensor, block: int, pr
     if out is None:
         out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
                   torch.empty(R * nb, dtype=torch.int32, device=q.device))
+    _check_csr(out, R, "out", q.device)
     ws = _workspace(shape, BSA_WS_STRUCTURED, 0, workspace, q.device)
     prm = BsaPatternParams(int(prefix_tokens), int(frame_tokens), int(band), int(period),
                            stripes.data_ptr() if stripes is not None and stripes.numel() else None,
                            int(stripes.numel()) if stripes is not None else 0)
     oc = out.c()
     st = load().bsa_structured_mask(ctypes.byref(shape), head_kind.data_ptr(), ctypes.byref(prm), ctypes.byref(oc),
-                                    ws.data_ptr(), ws.numel(), _stream())
+                                    ws.data_ptr(), _nbytes(ws), _stream())
     check(st, "bsa_structured_mask")
     return out
 
@@ -206,8 +233,8 @@ def bsa_permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = Fals
         raise ValueError("perm must be an int32 tensor of N entries on x's device")
     perm = perm.contiguous()
     out = torch.empty_like(x) if out is None else out
-    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like x")
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x on x's device")
     heads = x.shape[0] * x.shape[1]
     row_bytes = x.element_size() * (x.numel() // max(1, heads * n))
     st = load().bsa_permute_rows(int(heads), int(n), int(row_bytes), x.data_ptr(), perm.data_ptr(), int(bool(inverse)),
@@ -231,22 +258,21 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Csr, bl
     o = torch.empty_like(q) if out is None else out
     _check(o, "out", like=q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(lse, "lse", dtype=torch.float32)
+    _check(lse, "lse", dtype=torch.float32, shape=(B, H, N), device=q.device)
+    _check_csr(mask, num_rows(q, block), "mask", q.device)
     if want_mass and mass is None:
         mass = torch.empty(max(mask.capacity, 1), dtype=torch.float32, device=q.device)
     if mass is not None:
-        _check(mass, "mass", dtype=torch.float32)
+        _check(mass, "mass", dtype=torch.float32, device=q.device)
         if mass.numel() < mask.capacity:
             raise ValueError("mass must hold mask.capacity entries")
     if o32 is not None:
-        _check(o32, "o32", dtype=torch.float32)
-        if o32.shape != q.shape:
-            raise ValueError("o32 must have q's shape")
+        _check(o32, "o32", dtype=torch.float32, shape=q.shape, device=q.device)
     ws = _workspace(shape, BSA_WS_FORWARD, mask.capacity, workspace, q.device)
     mc = mask.c()
     st = load().bsa_forward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), float(scale),
                             ctypes.byref(mc), o.data_ptr(), lse.data_ptr(), _ptr(mass), _ptr(o32), ws.data_ptr(),
-                            ws.numel(), _stream())
+                            _nbytes(ws), _stream())
     check(st, "bsa_forward")
     return o, lse, (mass[: mask.capacity] if mass is not None else None)
 
@@ -258,20 +284,21 @@ def bsa_backward(q, k, v, o, d_o, lse, mask: Csr, block: int, scale: float = 0.0
     _check(q, "q")
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
         _check(t, n, like=q)
-    _check(lse, "lse", dtype=torch.float32)
     shape = _shape_of(q, block)
+    _check(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    _check_csr(mask, num_rows(q, block), "mask", q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, like=q)
     if o32 is not None:
-        _check(o32, "o32", dtype=torch.float32)
-        if o32.shape != q.shape:
-            raise ValueError("o32 must have q's shape")
+        _check(o32, "o32", dtype=torch.float32, shape=q.shape, device=q.device)
     ws = _workspace(shape, BSA_WS_BACKWARD, mask.capacity, workspace, q.device)
     mc = mask.c()
     st = load().bsa_backward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              _ptr(o32), d_o.data_ptr(), lse.data_ptr(), float(scale), ctypes.byref(mc), dq.data_ptr(),
-                             dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+                             dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
     check(st, "bsa_backward")
     return dq, dk, dv
 

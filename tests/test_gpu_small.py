@@ -243,6 +243,32 @@ def test_host_validation_errors(bsa):
     with pytest.raises(bsa.BsaError) as e:
         bsa.bsa_estimate_mask(q, q, 0.5, 32)
     assert e.value.status == 2
+    # caller-supplied outputs and masks the kernels would overrun are refused
+    # by the binding before any launch
+    mask = bsa.csr_from_host(np.array([0, 1, 2]), np.array([0, 0]), "cuda")   # 2 rows; q has 1 block per row
+    with pytest.raises(ValueError, match="lse"):
+        bsa.bsa_forward(q, q, q, mask, 64, lse=torch.empty((1, 1, 32), dtype=torch.float32, device="cuda"))
+    short = bsa.Csr(mask.row_ptr[:1], mask.col_idx)
+    with pytest.raises(ValueError, match="row_ptr"):
+        bsa.bsa_forward(q, q, q, short, 64)
+    with pytest.raises(ValueError, match="row_ptr"):
+        bsa.bsa_estimate_mask(q, q, 0.9, 64, out=short)
+    with pytest.raises(ValueError, match="col_idx"):
+        bsa.bsa_forward(q, q, q, bsa.Csr(mask.row_ptr, mask.col_idx.long()), 64)
+    o, lse, _ = bsa.bsa_forward(q, q, q, mask, 64)
+    with pytest.raises(ValueError, match="dk"):
+        bsa.bsa_backward(q, q, q, o, q, lse, mask, 64, dk=torch.empty((1, 1, 32, 64), dtype=torch.bfloat16,
+                                                                       device="cuda"))
+    # a workspace's size is its byte count, whatever its element type
+    need = bsa.bsa_workspace_size(bsa.make_shape(1, 1, 64, 64, 64, 0), 1, mask.capacity)
+    assert need > 8
+    o2, _, _ = bsa.bsa_forward(q, q, q, mask, 64, workspace=torch.empty(-(-need // 4), dtype=torch.float32,
+                                                                         device="cuda"))
+    assert torch.equal(o2, o)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_forward(q, q, q, mask, 64, workspace=torch.empty(need // 8, dtype=torch.float32, device="cuda"))
+    assert e.value.status == 3
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("dtype,delta", [("bf16", "exact"), ("bf16", "o32"), ("fp32", "exact")])
