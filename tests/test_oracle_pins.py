@@ -261,6 +261,74 @@ def test_narrow_by_mass_on_forward_masses():
             assert kept >= 0.8 * mass[rp[r]:rp[r + 1]].sum() - 1e-12
 
 
+def test_mass_top_p_negative_and_nan_masses_count_as_zero():
+    # entries 0, 1, 2, 3 with masses 0.6, -0.5, 0.4, NaN: the total is 1.0
+    # (the negative and the NaN count as 0), the ranking is 0, 2, then the two
+    # zero masses in ascending id, so C = 0.6, 1.0, 1.0, 1.0 and p = 0.9 keeps
+    # {0, 2}.  (Taking -0.5 at face value would give a total of 0.5 and keep
+    # {0} alone.)
+    sel = O.top_p_from_mass(np.array([0, 1, 2, 3]), np.array([0.6, -0.5, 0.4, np.nan]), 0.9)
+    assert sel.ranked.tolist() == [0, 2, 1, 3]
+    assert np.allclose(sel.cumulative, [0.6, 1.0, 1.0, 1.0], rtol=0, atol=1e-15)
+    assert sel.selected.tolist() == [0, 2]
+    # a row whose masses are all <= 0 has total 0 and keeps every entry
+    assert O.top_p_from_mass(np.array([3, 5]), np.array([-1.0, 0.0]), 0.5).selected.tolist() == [3, 5]
+
+
+def test_narrow_by_mass_ignores_ids_outside_the_grid():
+    # nb = 4: the row lists blocks 0, 5 and 1 with masses 0.2, 0.7 and 0.1.
+    # Block 5 does not exist, so the row is {0: 0.2, 1: 0.1}, total 0.3, and
+    # p = 0.6 keeps block 0 alone (C_1 = 2/3).  Counting block 5 would keep
+    # {5} instead.
+    rp, ci, _ = O.narrow_by_mass(np.array([0, 3]), np.array([0, 5, 1]), np.array([0.2, 0.7, 0.1]), 0.6, 0, 64, 4)
+    assert rp.tolist() == [0, 1] and ci.tolist() == [0]
+    rp, ci, _ = O.narrow_by_mass(np.array([0, 2]), np.array([-1, 2]), np.array([0.9, 0.1]), 0.5, 0, 64, 4)
+    assert rp.tolist() == [0, 1] and ci.tolist() == [2]
+
+
+def test_selection_band_hand_worked():
+    # The band excuses GPU/oracle differences: a block is in it when its
+    # logit is within tol of the cut seen from the other side, or when its
+    # inclusion hinges on a cumulative share within mass_tol of p; forced
+    # blocks never are.  Logits 2.0, 1.0, 1.0 + g, 0.0 for blocks 0..3 rank
+    # 0, 2, 1, 3; with e = exp: C_1 = e^2 / Z, C_2 = (e^2 + e^(1+g)) / Z.
+    def row(g, p, forced=()):
+        return O.top_p_select(np.arange(4), np.array([2.0, 1.0, 1.0 + g, 0.0]), p, np.array(forced, dtype=np.int64))
+
+    # p midway between C_1 ~ 0.534 and C_2 ~ 0.731: k* = 2, the cut lies
+    # between block 2 (kept) and block 1 (dropped), 5e-5 apart: both within
+    # 1e-4 of the other side, nothing near a cumulative share.
+    a = row(5e-5, 0.63)
+    assert a.k_star == 2 and a.selected.tolist() == [0, 2]
+    assert O.selection_band(a, 0.63) == {1, 2}
+    # 1.5e-4 apart: neither is within 1e-4 of the other side.
+    b = row(1.5e-4, 0.63)
+    assert b.k_star == 2 and O.selection_band(b, 0.63) == set()
+    # p just above C_2: k* = 3 (block 1 is kept because C_2 < p), and block 1
+    # is the rank-3 block whose inclusion hinges on C_2 being within 1e-5 of
+    # p; the value clause adds nothing (block 3 is 1.0 below block 1).
+    z = np.exp([2.0, 1.0, 1.0 + 1.5e-4, 0.0]).sum()
+    p = float((np.exp(2.0) + np.exp(1.0 + 1.5e-4)) / z + 1e-7)
+    c = row(1.5e-4, p)
+    assert c.k_star == 3 and O.selection_band(c, p) == {1}
+    # the same with block 1 forced: forced blocks are never in the band
+    assert O.selection_band(row(1.5e-4, p, forced=[1]), p) == set()
+    # p = 1 keeps every block and has no band
+    assert O.selection_band(row(5e-5, 1.0), 1.0) == set()
+
+
+def test_mass_band_hand_worked():
+    # entries 4, 7, 9 with masses 0.25, 0.5, 0.25 rank 7, 4, 9 (equal masses
+    # in ascending id), C = 0.5, 0.75, 1.0 exactly.  At p = 0.75 the rank-3
+    # block (9) is dropped only because C_2 reaches p exactly: it is the band.
+    sel = O.top_p_from_mass(np.array([4, 7, 9]), np.array([0.25, 0.5, 0.25]), 0.75)
+    assert sel.ranked.tolist() == [7, 4, 9] and sel.selected.tolist() == [4, 7]
+    assert O.mass_band(sel, 0.75) == {9}
+    assert O.mass_band(sel, 0.74) == set()
+    forced = O.top_p_from_mass(np.array([4, 7, 9]), np.array([0.25, 0.5, 0.25]), 0.75, np.array([9]))
+    assert O.mass_band(forced, 0.75) == set()
+
+
 # ----------------------------------------------------------------------------
 # token permutation
 # ----------------------------------------------------------------------------
