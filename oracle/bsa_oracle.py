@@ -285,8 +285,11 @@ def estimate_head(q: np.ndarray, k: np.ndarray, block: int, top_p: float, scale:
     forced = forced_blocks(keep_prefix_tokens, block, nb)
     rows = []
     for i in range(nb):
-        cand = np.arange(nb, dtype=np.int64) if candidate_rows is None else \
-            np.unique(np.asarray(candidate_rows[i], dtype=np.int64))
+        if candidate_rows is None:
+            cand = np.arange(nb, dtype=np.int64)
+        else:                                # repeated ids count once; ids outside [0, nb) are ignored
+            cand = np.unique(np.asarray(candidate_rows[i], dtype=np.int64))
+            cand = cand[(cand >= 0) & (cand < nb)]
         rows.append(top_p_select(cand, logits[i, cand], top_p, forced))
     return rows
 

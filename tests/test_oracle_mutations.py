@@ -48,6 +48,7 @@ MUTATIONS = [
      "    sel = np.union1d(ranked[:k_star], forced).astype(np.int64)\n    return RowSelection(cand,"),
     ("forced_ignored", "    sel = np.union1d(ranked[:k_star], forced).astype(np.int64)\n    return RowSelection(cand,",
      "    sel = np.sort(ranked[:k_star]).astype(np.int64)\n    return RowSelection(cand,"),
+    ("candidate_ids_unfiltered", "            cand = cand[(cand >= 0) & (cand < nb)]\n", ""),
     ("candidates_ignored", "rows.append(top_p_select(cand, logits[i, cand], top_p, forced))",
      "rows.append(top_p_select(np.arange(nb), logits[i], top_p, forced))"),
     # bands that excuse GPU/oracle differences

@@ -170,6 +170,12 @@ def test_candidate_restriction():
         assert r.selected.tolist() == sorted(set(keep) | {0})
     empty = O.estimate_head(q, k, bs, 0.8, 0.25, candidate_rows=[np.zeros(0)] * nb)
     assert all(r.selected.size == 0 for r in empty)
+    # repeated ids count once and ids outside [0, nb) are ignored (the CSR
+    # convention): such rows select what their distinct valid ids select
+    messy = [np.concatenate([[-3, -1], c, c[:2], [nb, nb + 7]]) for c in cands]
+    got = O.estimate_head(q, k, bs, 0.8, 0.25, candidate_rows=messy, keep_prefix_tokens=10)
+    assert [r.selected.tolist() for r in got] == [r.selected.tolist() for r in sub]
+    assert [r.candidates.tolist() for r in got] == [c.tolist() for c in cands]
 
 
 # ----------------------------------------------------------------------------
