@@ -416,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     uint32_t* __restrict__ bits, int words) {
   __shared__ uint32_t sel[kThreads / 64][kSortMax / 32];
   __shared__ uint32_t seen[kThreads / 64][kSortMax / 32];
+  __shared__ int32_t chunk_ids[kThreads / 64][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kThreads / 64) + wid;
   if (r >= R) return;                        // whole wavefront leaves together
@@ -431,6 +432,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     if (b > cand_cap) b = cand_cap;
     if (a < 0) a = 0;
     if (a > b) a = b;
+    if (b - a > (int64_t)EPL * 64) {
+      // More entries than distinct ids in [0, nb) can fill: the row starts
+      // with ignored negative ids (rows ascend).  Skip them (binary search,
+      // wave-uniform) so every valid id is among the entries read.
+      int64_t l = a, h = b;
+      while (l < h) {
+        const int64_t m = (l + h) >> 1;
+        if (cand_idx[m] < 0) l = m + 1; else h = m;
+      }
+      a = l;
+    }
     lo = a;
     n_c = (int)min<int64_t>(b - a, (int64_t)EPL * 64);
   } else {
@@ -447,23 +459,40 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     key[e] = 0u;                             // 0 = absent (finite logits order above 0)
     jj[e] = -1;
     sv[e] = 0.f;
+    int j = -1;
     if (t < n_c) {
-      const int j = cand_ptr ? cand_idx[lo + t] : t;
-      if (j >= 0 && j < nb) {
-        bool fresh = true;
-        if (cand_ptr) fresh = (atomicOr(&my_seen[j >> 5], 1u << (j & 31)) & (1u << (j & 31))) == 0u;
-        if (fresh) {
-          if constexpr (FROM_MASS) {
-            const float m = lrow[t];
-            sv[e] = m > 0.f ? m : 0.f;       // NaN compares false
-          } else {
-            sv[e] = lrow[j];
-          }
-          key[e] = ordered_bits(sv[e]);
-          jj[e] = j;
-          kmax = max(kmax, key[e]);
-        }
+      j = cand_ptr ? cand_idx[lo + t] : t;
+      if (j < 0 || j >= nb) j = -1;
+    }
+    bool fresh = j >= 0;
+    if (cand_ptr) {
+      // A block listed twice counts once, at its first listing.  Listings in
+      // earlier chunks are already in `seen`; two listings in this chunk race
+      // in the atomicOr, and when any lane loses such a race the lowest lane
+      // holding the id takes it, whatever order the atomics ran in.
+      bool lost = false;
+      if (fresh) {
+        const uint32_t bit = 1u << (j & 31);
+        fresh = (my_seen[j >> 5] & bit) == 0u;
+        lost = (atomicOr(&my_seen[j >> 5], bit) & bit) != 0u;
       }
+      if (__any(fresh && lost)) {
+        chunk_ids[wid][lane] = j;
+        __builtin_amdgcn_wave_barrier();
+        for (int l = 0; l < lane; ++l) fresh = fresh && chunk_ids[wid][l] != j;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    if (fresh) {
+      if constexpr (FROM_MASS) {
+        const float m = lrow[t];
+        sv[e] = m > 0.f ? m : 0.f;           // NaN compares false
+      } else {
+        sv[e] = lrow[j];
+      }
+      key[e] = ordered_bits(sv[e]);
+      jj[e] = j;
+      kmax = max(kmax, key[e]);
     }
   }
   kmax = wave_umax(kmax);

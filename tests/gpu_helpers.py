@@ -125,3 +125,27 @@ def compare_backward(x, block, rp, ci, scale, heads, grads_gpu, dtype: str):
             err["excess"] = max(err["excess"],
                                 float((diff - tol["grad"] - tol["store_rel"] * np.abs(want[0, 0])).max()))
     return err
+
+
+def messy_rows(rng, R: int, nb: int) -> list:
+    """Candidate / mask rows outside the strictly ascending form, for a grid of
+    65 <= nb <= 200 blocks (a row is then read up to 256 entries):
+      r % 4 == 0  repeats inside one 64-entry chunk (the first 10 ids twice);
+      r % 4 == 1  repeats across chunks, negative ids between the listings;
+      r % 4 == 2  ascending, 300 leading negative ids and 3 ids >= nb, so the
+                  row is longer than 256 entries;
+      r % 4 == 3  strictly ascending."""
+    assert 65 <= nb <= 200
+    rows = []
+    for r in range(R):
+        kind = r % 4
+        c = np.sort(rng.choice(nb, size=int(rng.integers(1, (60 if kind < 2 else nb) + 1)), replace=False))
+        if kind == 0:
+            rows.append(np.concatenate([c[:10], c[:10], c[10:]]))
+        elif kind == 1:
+            rows.append(np.concatenate([c, np.full(64 - c.size, -1), c]))
+        elif kind == 2:
+            rows.append(np.concatenate([np.arange(-300, 0), c, np.arange(nb, nb + 3)]))
+        else:
+            rows.append(c)
+    return rows

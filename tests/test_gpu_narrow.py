@@ -10,7 +10,7 @@ import torch
 
 from oracle import bsa_oracle as O
 from workloads import get, make_inputs
-from tests.gpu_helpers import default_scale, f32, to_device, to_host
+from tests.gpu_helpers import default_scale, f32, messy_rows, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +114,21 @@ def test_narrowing_empty_and_tiny_rows(bsa):
         _, _, sels = O.narrow_by_mass(rp, ci, mass.astype(np.float64), f32(p), keep, bs, nb)
         got = [gci[grp[r]:grp[r + 1]].tolist() for r in range(nb)]
         assert got == [s.selected.tolist() for s in sels], (p, keep)
+
+
+def test_narrowing_repeated_ids_and_long_rows(bsa):
+    """Rows that repeat ids (the first listing's mass counts, also when both
+    listings fall in one 64-entry chunk) or list ids outside [0, nb) (ignored,
+    also when they make the row longer than the entries a row is read up to)."""
+    nb, bs, H = 100, 64, 2
+    rng = np.random.default_rng(43)
+    rp, ci = O.rows_to_csr(messy_rows(rng, H * nb, nb))
+    mass = rng.random(ci.size).astype(np.float32)
+    for p in (0.5, 0.9):
+        grp, gci = _narrow_gpu(bsa, rp, ci, mass, f32(p), 0, 1, H, nb * bs - 5, bs)
+        _, _, sels = O.narrow_by_mass(rp, ci, mass.astype(np.float64), f32(p), 0, bs, nb)
+        bad, band = _compare(grp, gci, rp, ci, sels, nb, f32(p))
+        assert not bad, f"p={p}: {len(bad)} rows differ outside the band ({band} band blocks), first {bad[:5]}"
 
 
 @pytest.mark.parametrize("wl", ["tiny", "small128"])

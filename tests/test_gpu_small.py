@@ -222,6 +222,27 @@ def test_candidate_path_and_forced_prefix(bsa, dtype):
     assert ci[rp[2]:rp[3]].tolist() == [0, 1]
 
 
+def test_candidate_rows_with_repeats_and_out_of_grid_ids(bsa):
+    """Candidate rows select what their distinct ids in [0, nb) select:
+    repeats inside one 64-entry chunk and across chunks, and ascending rows
+    whose leading negative ids make them longer than the entries a row is
+    read up to."""
+    from tests.gpu_helpers import messy_rows
+    rng = np.random.default_rng(41)
+    B, H, N, D, bs = 1, 2, 100 * 64 - 5, 64, 64
+    q, k, v = _inputs(rng, B, H, N, D, "bf16", scale_q=0.3)
+    k = round_to_bf16(k + q)
+    nb = O.num_blocks(N, bs)
+    crp, cci = O.rows_to_csr(messy_rows(rng, B * H * nb, nb))
+    cand = bsa.csr_from_host(crp, cci, "cuda")
+    p = f32(0.85)
+    m = bsa.bsa_estimate_mask(to_device(q, "bf16"), to_device(k, "bf16"), p, bs, candidate=cand)
+    rp, ci = m.to_host()
+    _, _, sels = O.estimate_mask(q, k, bs, p, default_scale(D), candidate=(crp, cci))
+    rows, bad, band = compare_masks(rp, ci, sels, H, nb, p)
+    assert not bad, f"{len(bad)} of {rows} rows differ"
+
+
 def test_repeated_calls_are_bitwise_identical(bsa):
     w = get("tiny")
     x = make_inputs(w, dtype="bf16")
