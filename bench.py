@@ -1,12 +1,17 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-gsrs-loop]
+    python bench.py --cpu-full NAME [--cpu-threads T]     (CPU oracle only, whole workload)
 
 A step is one pass of the whole path over one batch of seeded synthetic
 video tokens already resident in HBM: the block-importance estimator
 (mean-pool, pooled scores, row softmax, Top-p, CSR) followed by the sparse
 forward with exact per-block attention mass (and, on the training workload,
-the backward).  Prints one JSON line.
+the backward).  The default workload is the largest single-GPU one, the
+HunyuanVideo-like layer (B 1, H 24, N 118,800, D 128, block 128).  Prints one
+JSON line; besides the step it times the reduced-search loop of the GSRS page
+(Figure 4 and Figure 7 captions) over the Wan2.1-like workload's five
+denoising steps.
 
 value = executed forward FLOP (4 D sum over selected pairs |Q_i||K_j|) per
 step divided by the step time, in TFLOP/s.  The roofline object reports the
@@ -81,19 +86,38 @@ def load_traffic(kernel: str, workload: str, flop_per_launch: float):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, scale, top_p, budget_s: float):
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(x, w, scale, top_p, budget_s: float, exec_flop_total: float):
     """Time the CPU oracle on a bounded, seeded sample of the workload.
 
     A third of the budget runs the oracle's estimator on whole heads (seeded
     order); the rest runs the oracle's forward on seeded rows of those heads,
     over the oracle's own masks.  The rate is the sampled rows' executed FLOP
-    over their forward time plus their share of the estimator time."""
+    over their forward time plus their share of the estimator time.  The
+    whole-workload time is extrapolated from the same sample: estimator time
+    per head times the heads, plus forward time per executed FLOP times the
+    workload's executed FLOP (taken from the GPU's mask)."""
     from oracle import bsa_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     rng = np.random.default_rng(12345)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     masks, t_est = [], 0.0
@@ -124,11 +148,168 @@ def cpu_baseline(x, w, scale, top_p, budget_s: float):
         if time.perf_counter() - t1 > budget_s * 2 / 3:
             break
     dt = t_fwd + n * est_per_row
+    whole = t_est / len(masks) * len(heads) + t_fwd / max(flop, 1.0) * exec_flop_total
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 numpy oracle: estimator on {len(masks)} of {len(heads)} heads ({t_est:.1f} s), "
-                      f"forward on {n} seeded rows of those heads over the oracle's masks ({t_fwd:.1f} s); "
-                      f"rate = their FLOP / (forward time + their share of the estimator time)",
+            "sample": f"float64 numpy oracle on {cpu_model()}: estimator on {len(masks)} of {len(heads)} heads "
+                      f"({t_est:.1f} s), forward on {n} seeded rows of those heads over the oracle's masks "
+                      f"({t_fwd:.1f} s); rate = their FLOP / (forward time + their share of the estimator time)",
+            "cpu_model": cpu_model(),
+            "whole_workload_s_extrapolated": round(whole, 1),
             "seconds": t_est + t_fwd, "rows": n}
+
+
+def cpu_full(name: str, threads: int) -> int:
+    """The whole oracle on one workload, on the host alone: the estimator on
+    every head, then the forward (O, LSE, block mass) on every row of its own
+    mask, and on the training workload the backward; every denoising step of a
+    multi-step workload (later steps searching step 1's blocks).  Prints one
+    JSON line with the seconds, the BLAS threads and the CPU model."""
+    from workloads import get, make_inputs
+    from oracle import bsa_oracle as O
+    w = get(name)
+    if threads > 0:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=threads)          # for the rest of this process
+    scale = float(np.float32(1.0 / np.sqrt(w.D)))
+    t_est = t_fwd = t_bwd = 0.0
+    flop = 0.0
+    cand = None
+    for s in range(1, w.steps + 1):
+        x = make_inputs(w, step=s, dtype="bf16", want_grad=w.backward)
+        p = float(np.float32(w.top_p[s - 1]))
+        ts = time.perf_counter()
+        rp, ci, _ = O.estimate_mask(x["q"], x["k"], w.block, p, scale, candidate=cand,
+                                    keep_prefix_tokens=w.keep_prefix_tokens)
+        t_est += time.perf_counter() - ts
+        print(json.dumps({"cpu_full": name, "step": s, "estimator_s": round(time.perf_counter() - ts, 2)}),
+              flush=True)
+        ts = time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.H):
+                r0 = (b * w.H + h) * w.nb
+                srp = rp[r0:r0 + w.nb + 1] - rp[r0]
+                sci = ci[rp[r0]:rp[r0 + w.nb]]
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                O.sparse_forward(x["q"][sl], x["k"][sl], x["v"][sl], w.block, srp, sci, scale)
+                if w.backward:
+                    tb = time.perf_counter()
+                    O.sparse_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl], w.block, srp, sci, scale)
+                    t_bwd += time.perf_counter() - tb
+                print(json.dumps({"cpu_full": name, "step": s, "head": [b, h], "elapsed_s":
+                                  round(time.perf_counter() - ts, 1)}), file=sys.stderr, flush=True)
+        t_fwd += time.perf_counter() - ts
+        flop += 4.0 * w.D * executed_pairs(w.N, w.block, w.B * w.H, rp, ci)
+        if w.reduced_search and s == 1:
+            cand = (rp, ci)
+    t_fwd -= t_bwd
+    print(json.dumps({"cpu_full": name, "kind": "oracle", "cores": threads if threads > 0 else blas_threads(),
+                      "cpu_model": cpu_model(), "steps": w.steps, "estimator_s": round(t_est, 2),
+                      "forward_s": round(t_fwd, 2), "backward_s": round(t_bwd, 2) if w.backward else None,
+                      "total_s": round(t_est + t_fwd + t_bwd, 2), "executed_fwd_tflop": flop / 1e12,
+                      "fwd_tflops": round(flop / max(t_fwd, 1e-9) / 1e12, 5)}), flush=True)
+    return 0
+
+
+def gsrs_loop(torch, bsa, dev, reps: int) -> dict:
+    """The reduced-search loop of the GSRS page (Figure 4 caption: search steps
+    restricted to the baseline mask, then reuse; Figure 7 caption: search
+    overhead) over the Wan2.1-like workload's five denoising steps.
+
+    Step 1 is a full search (estimator over every block) and a forward with
+    exact block mass.  Steps 2-5 each narrow the previous step's mask by its
+    block masses at the step's Top-p (bsa_select_from_mass) and run the forward
+    with mass on the narrowed mask; the reduced-search estimator (scoring only
+    step 1's blocks) is timed beside them at the same Top-p.  A final
+    non-search step reuses step 5's mask for a forward alone.  Times are HIP
+    events on the library's stream, the mean of ``reps`` passes over the loop
+    (after one untimed pass)."""
+    from workloads import get, make_inputs, bf16_bits
+    w = get("wan")
+
+    def up(arr):
+        return torch.from_numpy(bf16_bits(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    steps = []
+    for s in range(1, w.steps + 1):
+        x = make_inputs(w, step=s, dtype="bf16")
+        steps.append(tuple(up(x[n]) for n in "qkv"))
+        del x
+    R, cap = w.B * w.H * w.nb, w.B * w.H * w.nb * w.nb
+    shape = bsa.make_shape(w.B, w.H, w.N, w.D, w.block, 0)
+    ws_e = torch.empty(bsa.bsa_workspace_size(shape, 0, 0), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(bsa.bsa_workspace_size(shape, 1, cap), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(bsa.bsa_workspace_size(shape, 3, 0), dtype=torch.uint8, device=dev)
+    masks = [bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int32,
+                                                                                     device=dev))
+             for _ in range(w.steps)]
+    red = bsa.Csr(torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int32, device=dev))
+    masses = [torch.empty(cap, dtype=torch.float32, device=dev) for _ in range(w.steps)]
+    o = torch.empty_like(steps[0][0])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ps = [float(np.float32(p)) for p in w.top_p]
+    names = ["search"] + ["narrow"] * (w.steps - 1)
+    acc = {k: np.zeros(w.steps) for k in ("search_ms", "fwd_ms", "reduced_ms")}
+    reuse_ms = loop_ms = 0.0
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    for rep in range(reps + 1):
+        marks = []
+        t_loop0 = ev()
+        for s in range(w.steps):
+            q, k, v = steps[s]
+            a = ev()
+            if s == 0:
+                bsa.bsa_estimate_mask(q, k, ps[0], w.block, out=masks[0], workspace=ws_e)
+            else:
+                bsa.bsa_select_from_mass(q, masks[s - 1], masses[s - 1], ps[s], w.block, out=masks[s],
+                                         workspace=ws_s)
+            b = ev()
+            bsa.bsa_forward(q, k, v, masks[s], w.block, out=o, lse=lse, mass=masses[s], workspace=ws_f)
+            c = ev()
+            marks.append((a, b, c))
+        q, k, v = steps[-1]
+        r0 = ev()
+        bsa.bsa_forward(q, k, v, masks[-1], w.block, want_mass=False, out=o, lse=lse, workspace=ws_f)
+        r1 = ev()
+        t_loop1 = ev()
+        red_marks = []
+        for s in range(1, w.steps):                      # reduced search beside the narrowing
+            q, k, _ = steps[s]
+            a = ev()
+            bsa.bsa_estimate_mask(q, k, ps[s], w.block, candidate=masks[0], out=red, workspace=ws_e)
+            red_marks.append((a, ev()))
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue
+        for s, (a, b, c) in enumerate(marks):
+            acc["search_ms"][s] += a.elapsed_time(b) / reps
+            acc["fwd_ms"][s] += b.elapsed_time(c) / reps
+        for s, (a, b) in enumerate(red_marks, start=1):
+            acc["reduced_ms"][s] += a.elapsed_time(b) / reps
+        reuse_ms += r0.elapsed_time(r1) / reps
+        loop_ms += t_loop0.elapsed_time(t_loop1) / reps
+    nnz = [int(m.row_ptr[-1].item()) for m in masks]
+    full = acc["search_ms"][0]
+    narrow = float(np.mean(acc["search_ms"][1:]))
+    reduced = float(np.mean(acc["reduced_ms"][1:]))
+    out = {"workload": f"{w.name}: {w.note}", "top_p": [round(p, 4) for p in ps],
+           "steps": [{"step": s + 1, "search": names[s], "search_ms": round(acc["search_ms"][s], 4),
+                      "fwd_mass_ms": round(acc["fwd_ms"][s], 4), "nnz": nnz[s],
+                      "block_density": round(nnz[s] / (R * w.nb), 4)} for s in range(w.steps)],
+           "reduced_search_ms": [round(t, 4) for t in acc["reduced_ms"][1:]],
+           "reuse_step_fwd_ms": round(reuse_ms, 4),
+           "loop_ms": round(loop_ms, 4),
+           "search_overhead_ratio_full_vs_narrow": round(full / narrow, 2),
+           "search_overhead_ratio_full_vs_reduced": round(full / reduced, 2),
+           "search_share_of_loop": round((full + narrow * (w.steps - 1)) / loop_ms, 4)}
+    del steps, masks, masses, red, ws_e, ws_f, ws_s, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def density_sweep(torch, bsa, steps: int, warmup: int) -> int:
@@ -184,8 +365,13 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="cogvideox")
+    ap.add_argument("--workload", default="hunyuan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gsrs-loop", action="store_true",
+                    help="skip the reduced-search loop over the Wan2.1-like workload's five steps")
+    ap.add_argument("--cpu-full", metavar="WORKLOAD", default=None,
+                    help="run only the whole CPU oracle on WORKLOAD (no GPU) and print its time")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="BLAS threads for --cpu-full (0: all)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--density-sweep", action="store_true",
                     help="instead of the step: forward latency and TFLOP/s over seeded random block masks of "
@@ -194,6 +380,8 @@ def main(argv=None) -> int:
                     help="after the timed region, run one plain device-to-device copy of BYTES bytes "
                          "(reference point for HBM byte counters under rocprofv3 --pmc)")
     a = ap.parse_args(argv)
+    if a.cpu_full:
+        return cpu_full(a.cpu_full, a.cpu_threads)
     if a.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1 (the path shards over "
                                    "heads with no exchange, and no multi-GPU run is implemented)"}))
@@ -436,9 +624,14 @@ def main(argv=None) -> int:
     if w.backward:
         out["bwd_ms"] = round(bwd_ms, 4)
         out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)
+    if not a.no_gsrs_loop:
+        print("bench: reduced-search loop over the Wan2.1-like steps", file=sys.stderr, flush=True)
+        out["gsrs_loop"] = gsrs_loop(torch, bsa, dev, reps=3)
     if not a.no_cpu_baseline:
-        cb = cpu_baseline(x, w, scale, top_p, a.cpu_budget)
-        out["cpu_baseline"] = {k2: cb[k2] for k2 in ("value", "unit", "cores", "kind", "sample")}
+        print("bench: CPU oracle sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(x, w, scale, top_p, a.cpu_budget, exec_flop)
+        out["cpu_baseline"] = {k2: cb[k2] for k2 in ("value", "unit", "cores", "kind", "sample", "cpu_model",
+                                                      "whole_workload_s_extrapolated")}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

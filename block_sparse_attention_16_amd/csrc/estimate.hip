@@ -21,7 +21,9 @@
 //                   lower block id, forced prefix blocks; the selection of
 //                   64 blocks is one ballot -> selection bitmask
 //   select_kernel   the same rule over each row's candidate blocks (reduced
-//                   search) -> selection bitmask
+//                   search); the whole CSR row is streamed through a
+//                   per-wavefront bitmask indexed by block id, so repeats
+//                   count once -> selection bitmask
 //   csr_kernel      per workgroup of 8 rows: sum of the earlier rows' counts,
 //                   scan of its own -> CSR row_ptr; bitmasks -> ascending
 //                   col_idx (one wavefront per 2 rows, 64 blocks per store)
@@ -299,45 +301,33 @@ __device__ __forceinline__ constexpr bool isolation_check(int bit) {
   return bit == 20 || bit == 16 || bit == 12 || bit == 8;
 }
 
-// Full search (no candidate rows), one mask row per wavefront, 4 per
-// workgroup: lane l holds blocks j = 64e + l, e < EPL.  Same Top-p rule as
-// select_kernel below (bisection for the cut logit L*, blocks above it kept,
-// blocks at L* added in ascending id until the mass reaches p * Z), with
-// every per-block decision in registers: the selection of element e is one
-// ballot, whose two halves are bitmask words 2e and 2e + 1.
+// Top-p over one mask row held in registers, one row per wavefront: lane l
+// holds blocks j = 64e + l, e < EPL.  key[e] is the order-preserving bit
+// pattern of the block's sort value (its logit, or its mass when narrowing),
+// 0 for a block that is not a candidate; ev[e] is its weight, exp(s - max)
+// or the mass (0 when absent).  With M(T) = sum of the weights of blocks whose
+// key is >= T and Z = M(1), the cut key L* is the largest T with
+// M(T) >= p Z, found bit by bit from the top; every block above L* is kept,
+// and blocks exactly at L* are added in ascending id until the mass reaches
+// p Z.  That is the shortest prefix of the (value desc, id asc) ranking whose
+// cumulative share reaches p, summed in another order.  Forced blocks
+// (j < n_forced) join after the cut.  The selection of element e is one
+// ballot, whose halves are bitmask words 2e and 2e + 1.
 template <int EPL>
-__global__ __launch_bounds__(kThreads) void select_full_kernel(const float* __restrict__ logits, int nb, int R,
-                                                               float top_p, int n_forced,
-                                                               int32_t* __restrict__ counts,
-                                                               uint32_t* __restrict__ bits, int words) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (r >= R) return;                        // whole wavefront leaves together
-  const float* lrow = logits + (size_t)r * nb;
-  uint32_t key[EPL];                         // ordered logit bits; 0 = no block
-  float ev[EPL];
-  uint32_t kmax = 0u;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int t = e * 64 + lane;
-    const bool ok = t < nb;
-    const float sv = lrow[ok ? t : 0];
-    key[e] = ok ? ordered_bits(sv) : 0u;
-    ev[e] = sv;
-    kmax = max(kmax, key[e]);
-  }
-  kmax = wave_umax(kmax);
-  const float smax = unordered_bits(kmax);
+__device__ __forceinline__ void select_row(const uint32_t (&key)[EPL], const float (&ev)[EPL], float top_p,
+                                           int nb, int n_forced, int r, int32_t* __restrict__ counts,
+                                           uint32_t* __restrict__ bits, int words, int lane) {
   float zl = 0.f;
+  bool any = false;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    ev[e] = key[e] ? __builtin_amdgcn_exp2f((ev[e] - smax) * kLog2e) : 0.f;
     zl += ev[e];
+    any = any || key[e] != 0u;
   }
   const float Z = uniform(wave_sum(zl));
-  uint32_t cut = 1u;                         // keep every block by default
+  uint32_t cut = 1u;                         // keep every present block by default
   int k_tie = -1;                            // >= 0: tied blocks at the cut to add
-  if (top_p < 1.0f && Z > 0.f) {
+  if (top_p < 1.0f && Z > 0.f && __any(any)) {
     const float thr = top_p * Z;
     uint32_t T = 0u;
 #pragma unroll
@@ -397,182 +387,107 @@ __global__ __launch_bounds__(kThreads) void select_full_kernel(const float* __re
   if (lane == 0) counts[r] = cnt;
 }
 
-// One mask row per wavefront (4 rows per workgroup).  Lane l holds candidate
-// positions t = e*64 + l, e < EPL.  Top-p: with e_j = exp(s_j - max) and
-// M(T) = sum of e_j over ordered(s_j) >= T, the cut logit L* is the largest T
-// with M(T) >= p * Z, found bit by bit from the top; every block above L* is
-// kept and blocks exactly at L* are added in ascending id until the mass
-// reaches p * Z.  This is the shortest prefix of the (logit desc, id asc)
-// ranking whose cumulative probability reaches p, summed in another order.
-//
-// FROM_MASS: `logits` is a [capacity] array of block masses aligned with
-// cand_idx (cand_ptr is required); the weight of a block is its mass (a
-// negative or NaN mass counts as 0) and ranking is by mass.  A row whose
-// masses sum to 0 keeps every entry.
+// Weights exp(s - max) of a row of logits held as (key, value) pairs; absent
+// blocks (key 0) get weight 0.
+template <int EPL>
+__device__ __forceinline__ void softmax_weights(const uint32_t (&key)[EPL], float (&ev)[EPL]) {
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) kmax = max(kmax, key[e]);
+  kmax = wave_umax(kmax);
+  const float smax = kmax ? unordered_bits(kmax) : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ev[e] = key[e] ? __builtin_amdgcn_exp2f((ev[e] - smax) * kLog2e) : 0.f;
+}
+
+// Full search (every block a candidate): one mask row per wavefront, 4 per
+// workgroup, the row's pooled logits read from `logits` [R, nb].
+template <int EPL>
+__global__ __launch_bounds__(kThreads) void select_full_kernel(const float* __restrict__ logits, int nb, int R,
+                                                               float top_p, int n_forced,
+                                                               int32_t* __restrict__ counts,
+                                                               uint32_t* __restrict__ bits, int words) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;                        // whole wavefront leaves together
+  const float* lrow = logits + (size_t)r * nb;
+  uint32_t key[EPL];                         // ordered logit bits; 0 = no block
+  float ev[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int t = e * 64 + lane;
+    const bool ok = t < nb;
+    const float sv = lrow[ok ? t : 0];
+    key[e] = ok ? ordered_bits(sv) : 0u;
+    ev[e] = sv;
+  }
+  softmax_weights<EPL>(key, ev);
+  select_row<EPL>(key, ev, top_p, nb, n_forced, r, counts, bits, words, lane);
+}
+
+// Rows read from a CSR over the same R rows (one row per wavefront, 4 per
+// workgroup), every entry of a row, in chunks of 64: reduced search scores
+// only the blocks a row lists (the softmax is over them alone); narrowing
+// (FROM_MASS) ranks them by the block masses aligned with the CSR entries.
+// A block id marks its slot (lane j % 64, element j / 64) in a per-wavefront
+// LDS bitmask, so repeats count once whatever their order; FROM_MASS keeps
+// the first listing's position with an LDS atomicMin and reads that entry's
+// mass (a negative or NaN mass counts as 0).  Ids outside [0, nb) and entries
+// at or past cand_cap are ignored; a row is read up to 2^31 - 1 entries.
 template <int EPL, bool FROM_MASS>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ logits, int nb, int R, float top_p, const int32_t* __restrict__ cand_ptr,
     const int32_t* __restrict__ cand_idx, int64_t cand_cap, int n_forced, int32_t* __restrict__ counts,
     uint32_t* __restrict__ bits, int words) {
-  __shared__ uint32_t sel[kThreads / 64][kSortMax / 32];
-  __shared__ uint32_t seen[kThreads / 64][kSortMax / 32];
-  __shared__ int32_t chunk_ids[kThreads / 64][64];
+  constexpr int L = EPL * 64;                // block slots of a row
+  constexpr int NF = FROM_MASS ? L : 1;
+  __shared__ uint32_t seen[kThreads / 64][L / 32];
+  __shared__ int32_t first[kThreads / 64][NF];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kThreads / 64) + wid;
   if (r >= R) return;                        // whole wavefront leaves together
-  uint32_t* my_sel = sel[wid];
   uint32_t* my_seen = seen[wid];
-  for (int w = lane; w < words; w += 64) { my_sel[w] = 0u; my_seen[w] = 0u; }
+  int32_t* my_first = first[wid];
+  for (int w = lane; w < L / 32; w += 64) my_seen[w] = 0u;
+  if constexpr (FROM_MASS)
+    for (int t = lane; t < L; t += 64) my_first[t] = 0x7fffffff;
   __builtin_amdgcn_wave_barrier();
 
-  int n_c;
-  int64_t lo = 0;
-  if (cand_ptr) {
-    int64_t a = cand_ptr[r], b = cand_ptr[r + 1];
-    if (b > cand_cap) b = cand_cap;
-    if (a < 0) a = 0;
-    if (a > b) a = b;
-    if (b - a > (int64_t)EPL * 64) {
-      // More entries than distinct ids in [0, nb) can fill: the row starts
-      // with ignored negative ids (rows ascend).  Skip them (binary search,
-      // wave-uniform) so every valid id is among the entries read.
-      int64_t l = a, h = b;
-      while (l < h) {
-        const int64_t m = (l + h) >> 1;
-        if (cand_idx[m] < 0) l = m + 1; else h = m;
-      }
-      a = l;
-    }
-    lo = a;
-    n_c = (int)min<int64_t>(b - a, (int64_t)EPL * 64);
-  } else {
-    n_c = nb;
-  }
-  const float* lrow = FROM_MASS ? logits + lo : logits + (size_t)r * nb;
-  uint32_t key[EPL];
-  int jj[EPL];
-  float sv[EPL];
-  uint32_t kmax = 0u;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int t = e * 64 + lane;
-    key[e] = 0u;                             // 0 = absent (finite logits order above 0)
-    jj[e] = -1;
-    sv[e] = 0.f;
-    int j = -1;
-    if (t < n_c) {
-      j = cand_ptr ? cand_idx[lo + t] : t;
-      if (j < 0 || j >= nb) j = -1;
-    }
-    bool fresh = j >= 0;
-    if (cand_ptr) {
-      // A block listed twice counts once, at its first listing.  Listings in
-      // earlier chunks are already in `seen`; two listings in this chunk race
-      // in the atomicOr, and when any lane loses such a race the lowest lane
-      // holding the id takes it, whatever order the atomics ran in.
-      bool lost = false;
-      if (fresh) {
-        const uint32_t bit = 1u << (j & 31);
-        fresh = (my_seen[j >> 5] & bit) == 0u;
-        lost = (atomicOr(&my_seen[j >> 5], bit) & bit) != 0u;
-      }
-      if (__any(fresh && lost)) {
-        chunk_ids[wid][lane] = j;
-        __builtin_amdgcn_wave_barrier();
-        for (int l = 0; l < lane; ++l) fresh = fresh && chunk_ids[wid][l] != j;
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-    if (fresh) {
-      if constexpr (FROM_MASS) {
-        const float m = lrow[t];
-        sv[e] = m > 0.f ? m : 0.f;           // NaN compares false
-      } else {
-        sv[e] = lrow[j];
-      }
-      key[e] = ordered_bits(sv[e]);
-      jj[e] = j;
-      kmax = max(kmax, key[e]);
+  int64_t a = cand_ptr[r], b = cand_ptr[r + 1];
+  if (b > cand_cap) b = cand_cap;
+  if (a < 0) a = 0;
+  if (a > b) a = b;
+  const int n = (int)min<int64_t>(b - a, 0x7fffffff);
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    const int j = t < n ? cand_idx[a + t] : -1;
+    if (j >= 0 && j < nb) {
+      atomicOr(&my_seen[j >> 5], 1u << (j & 31));
+      if constexpr (FROM_MASS) atomicMin(&my_first[j], t);
     }
   }
-  kmax = wave_umax(kmax);
-  const float smax = kmax ? unordered_bits(kmax) : 0.f;
-  float ev[EPL];
-  float zl = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    if constexpr (FROM_MASS) ev[e] = sv[e];
-    else ev[e] = key[e] ? expf(sv[e] - smax) : 0.f;
-    zl += ev[e];
-  }
-  const float Z = wave_sum(zl);
-  uint32_t cut = 1u;                         // keep every present block by default
-  bool tie_walk = false;
-  if (top_p < 1.0f && kmax != 0u && Z > 0.f) {
-    const float thr = top_p * Z;
-    uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      float m = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) m += key[e] >= c ? ev[e] : 0.f;
-      if (wave_sum(m) >= thr) T = c;
-      if (isolation_check(bit) && isolated_cut<EPL>(key, T, bit, T)) break;
-    }
-    cut = T;                                 // L*: M(L*) >= p Z > M(L* + 1)
-    int nt = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) nt += key[e] == T ? 1 : 0;
-    tie_walk = wave_sum_i(nt) > 1;
-    if (tie_walk) {
-      // several blocks share the cut logit: add them in ascending id
-      float mg = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) mg += key[e] > T ? ev[e] : 0.f;
-      const float m_gt = wave_sum(mg);
-      float etie = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) if (key[e] == T) etie = ev[e];
-      etie = wave_fmax(etie);
-      // mark the tied ids, then one lane walks them in ascending order
-      for (int w = lane; w < words; w += 64) my_seen[w] = 0u;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        if (key[e] == T) atomicOr(&my_seen[jj[e] >> 5], 1u << (jj[e] & 31));
-      __builtin_amdgcn_wave_barrier();
-      if (lane == 0) {
-        float acc = m_gt;
-        bool done = false;
-        for (int w = 0; w < words && !done; ++w) {
-          uint32_t b = my_seen[w];
-          while (b && !done) {
-            const int bit = __ffs(b) - 1;
-            b &= b - 1;
-            my_sel[w] |= 1u << bit;
-            acc += etie;
-            done = acc >= thr;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const bool take = key[e] != 0u && (tie_walk ? key[e] > cut : key[e] >= cut);
-    if (take) atomicOr(&my_sel[jj[e] >> 5], 1u << (jj[e] & 31));
-  }
-  for (int j = lane; j < n_forced; j += 64) atomicOr(&my_sel[j >> 5], 1u << (j & 31));
   __builtin_amdgcn_wave_barrier();
-  int cnt = 0;
-  for (int w = lane; w < words; w += 64) {
-    const uint32_t bw = my_sel[w];
-    bits[(size_t)r * words + w] = bw;
-    cnt += __popc(bw);
+
+  uint32_t key[EPL];
+  float ev[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int j = e * 64 + lane;
+    const bool present = j < nb && ((my_seen[j >> 5] >> (j & 31)) & 1u);
+    float sv = 0.f;
+    if (present) {
+      if constexpr (FROM_MASS) {
+        const float m = logits[a + my_first[j]];
+        sv = m > 0.f ? m : 0.f;              // NaN compares false
+      } else {
+        sv = logits[(size_t)r * nb + j];
+      }
+    }
+    key[e] = present ? ordered_bits(sv) : 0u;  // finite values order above 0
+    ev[e] = sv;
   }
-  cnt = wave_sum_i(cnt);
-  if (lane == 0) counts[r] = cnt;
+  if constexpr (!FROM_MASS) softmax_weights<EPL>(key, ev);
+  select_row<EPL>(key, ev, top_p, nb, n_forced, r, counts, bits, words, lane);
 }
 
 // CSR assembly in one launch.  Workgroup b takes rows [8b, 8b + 8): it sums

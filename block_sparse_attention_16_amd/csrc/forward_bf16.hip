@@ -55,6 +55,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
@@ -220,13 +221,20 @@ __device__ __forceinline__ void scores_only(const char* ks, const bf16x8 (&qf)[C
 }
 
 // Probabilities j in [j0, j1) of the current unit: exp2 of the scaled,
-// max-shifted scores (in place), their running sum, and bf16 copies (pairs)
-// for the PV MFMAs.
+// max-shifted scores (in place), their running sum ls, and bf16 copies
+// (pairs) for the PV MFMAs with the running sum lt of those rounded copies
+// (one v_dot2 against (1, 1) per pair).  O is normalised by lt, the weights
+// its PV product actually used, so that O is a weighted mean of V rows and
+// the rounding of P moves it only by the weighted spread of V around O;
+// normalising by ls instead lets the rounding of the largest probabilities
+// scale O as a whole (up to ~2.5 times the error on the video workloads).
+// LSE and block mass use the exact sum ls.
 // With max_under_pv the scores are overwritten by their probabilities;
 // otherwise they are kept for a possible second pass (rescale_redo).
 template <int BS, int D, class C = Cfg<BS, D>>
 __device__ __forceinline__ void probs(floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float c2, float m_use,
-                                      float& ls, int j0, int j1) {
+                                      float& ls, float& lt, int j0, int j1) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float prev = 0.f;
 #pragma unroll
   for (int j = j0; j < j1; ++j) {
@@ -236,13 +244,17 @@ __device__ __forceinline__ void probs(floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC]
     if constexpr (max_under_pv<D>()) {
       sc[t][v2] = p;
       if (j & 1) {
-        pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)sc[t][v2 - 1];
-        pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+        const bf16x2 pr = {(__bf16)sc[t][v2 - 1], (__bf16)p};
+        pb[t][v2 / 8][(v2 - 1) % 8] = pr[0];
+        pb[t][v2 / 8][v2 % 8] = pr[1];
+        lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
       }
     } else {
       if (j & 1) {
-        pb[t][v2 / 8][(v2 - 1) % 8] = (__bf16)prev;
-        pb[t][v2 / 8][v2 % 8] = (__bf16)p;
+        const bf16x2 pr = {(__bf16)prev, (__bf16)p};
+        pb[t][v2 / 8][(v2 - 1) % 8] = pr[0];
+        pb[t][v2 / 8][v2 % 8] = pr[1];
+        lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
       }
       prev = p;
     }
@@ -256,7 +268,7 @@ __device__ __forceinline__ void probs(floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC]
 template <int BS, int D, bool NEXT, class C = Cfg<BS, D>>
 __device__ __forceinline__ void phase_b(const char* ks, const bf16x8 (&qf)[C::DS], floatx16 (&sc)[C::KC],
                                         floatx16 (&sn)[C::KC], bf16x8 (&pb)[C::KC][2], float c2, float m_use,
-                                        float& ls, int l32, int hf) {
+                                        float& ls, float& lt, int l32, int hf) {
   constexpr int NS = C::DS * C::KC;            // score MFMAs of the next unit
   constexpr int NE = C::KC * 16;               // probabilities per lane
   constexpr int NSEG = NEXT ? NS : 1;
@@ -276,7 +288,7 @@ __device__ __forceinline__ void phase_b(const char* ks, const bf16x8 (&qf)[C::DS
       const int ds = g / C::KC, t = g % C::KC;
       sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ds], ds == 0 ? zero : sn[t], 0, 0, 0);
     }
-    probs<BS, D>(sc, pb, c2, m_use, ls, g * EPS, (g + 1) * EPS < NE ? (g + 1) * EPS : NE);
+    probs<BS, D>(sc, pb, c2, m_use, ls, lt, g * EPS, (g + 1) * EPS < NE ? (g + 1) * EPS : NE);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -367,6 +379,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  float lt_run = 0.f;      // running sum of the bf16-rounded probabilities (normalises O)
   float ls_blk = 0.f;      // current entry's sum of exp2(s - m_run), for the block mass
   const float c2 = scale * kLog2e;   // logits in base-2 units
 
@@ -416,13 +429,15 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 #pragma unroll
         for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
       l_run *= alpha;
+      lt_run *= alpha;
       ls_blk *= alpha;
     }
   };
   // D = 128: the unit's probabilities overflowed the safe range, or nothing
   // is accumulated yet: fold in the unit's exact max, rescale what is
   // accumulated (nothing when m_run was -inf), take the probabilities again.
-  auto rescale_redo = [&](floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float& ls) __attribute__((always_inline)) {
+  auto rescale_redo = [&](floatx16 (&sc)[C::KC], bf16x8 (&pb)[C::KC][2], float& ls, float& lt)
+                          __attribute__((always_inline)) {
     const float m_new = fmaxf(m_run, xhalf_max(unit_max(sc)) * c2);
     if (m_new != m_run) {
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -431,11 +446,13 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 #pragma unroll
         for (int v2 = 0; v2 < 16; ++v2) acc[dt][v2] *= alpha;
       l_run *= alpha;
+      lt_run *= alpha;
       ls_blk *= alpha;
       m_run = m_new;
     }
     ls = 0.f;
-    probs<BS, D>(sc, pb, c2, m_run == -INFINITY ? 0.f : m_run, ls, 0, C::KC * 16);
+    lt = 0.f;
+    probs<BS, D>(sc, pb, c2, m_run == -INFINITY ? 0.f : m_run, ls, lt, 0, C::KC * 16);
   };
 
   floatx16 sa[C::KC], sb[C::KC];     // scores of the current and the next unit
@@ -475,13 +492,14 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     jv2 = col_load(u + 3);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pb[C::KC][2];
-    float ls = 0.f;
-    phase_b<BS, D, NEXT>(ks_next, qf, sc, sn, pb, c2, m_use, ls, l32, hf);
+    float ls = 0.f, lt = 0.f;
+    phase_b<BS, D, NEXT>(ks_next, qf, sc, sn, pb, c2, m_use, ls, lt, l32, hf);
     if constexpr (!max_under_pv<D>()) {
-      if (__any(m_run == -INFINITY || ls > kSumMax)) rescale_redo(sc, pb, ls);
+      if (__any(m_run == -INFINITY || ls > kSumMax)) rescale_redo(sc, pb, ls, lt);
     }
     ls = xhalf_sum(ls);
     l_run += ls;
+    lt_run += xhalf_sum(lt);
     ls_blk += ls;
     if (u % C::U == C::U - 1) {         // last unit of the entry
       const int it = u / C::U;
@@ -506,7 +524,7 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   if (u < n_u) iter(No{}, u, sa, sb, k1s, v0s, k0s, v1s);
 
   // ---- normalise, write O and LSE ----
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = l_run > 0.f && lt_run > 0.f ? 1.f / lt_run : 0.f;
   const float mu = m_run == -INFINITY ? 0.f : m_run;
   const float lse2 = l_run > 0.f ? mu + __builtin_amdgcn_logf(l_run) : -INFINITY;
   if (hf == 0) lse2_s[qloc] = lse2;

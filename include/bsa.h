@@ -99,9 +99,9 @@ size_t bsa_workspace_size(const bsa_shape* shape, int32_t kind, int64_t capacity
  *   candidate  NULL: every key block is scored.  Otherwise a CSR over the same
  *              R rows; row r scores, softmaxes and ranks only its candidate
  *              blocks (reduced search).  An empty candidate row selects only
- *              the forced blocks.  Repeated ids count once; rows longer than
- *              L entries are read as in bsa_select_from_mass.
- *              Must not alias `out`.
+ *              the forced blocks.  Every entry of a row is read (up to
+ *              2^31 - 1 per row), in any order; repeated ids count once and
+ *              ids outside [0, nb) are ignored.  Must not alias `out`.
  *   keep_prefix_tokens  in [0, N]: key blocks j with j*block < keep_prefix_tokens
  *              (e.g. a text prefix) join every row after the Top-p cut.
  *   out        CSR written by the call.  out->row_ptr receives exact offsets
@@ -151,11 +151,9 @@ bsa_status bsa_estimate_mask_hierarchical(const bsa_shape* shape, const void* q,
  *   block_mass [mask->capacity] fp32 device array aligned with mask->col_idx,
  *              e.g. bsa_forward's block_mass.  A negative or NaN mass counts
  *              as 0; a row whose masses sum to 0 keeps every entry; a block
- *              listed twice in a row counts once, with its first mass.  A row
- *              is read up to L entries, L the smallest of 64, 256, 1024 and
- *              4096 that is >= nb; a longer row (only possible with ids
- *              outside [0, nb) or repeated ids) is read from its first
- *              non-negative id on, up to L entries.
+ *              listed twice in a row counts once, with the mass of its first
+ *              listing; ids outside [0, nb) are ignored.  Every entry of a
+ *              row is read (up to 2^31 - 1 per row), in any order.
  *   top_p      in (0, 1]; 1 keeps every entry.
  *   out        CSR written by the call (a subset of mask plus forced blocks),
  *              rows ascending; exact row_ptr offsets, entries past

@@ -57,13 +57,17 @@ def compare_masks(rp_gpu, ci_gpu, sels: dict, H: int, nb: int, top_p: float, can
     return rows, bad, band_total
 
 
-def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass_gpu, dtype: str):
-    """Oracle on the GPU's own mask for the listed rows; returns the max errors."""
+def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass_gpu, dtype: str, o32_gpu=None):
+    """Oracle on the GPU's own mask for the listed rows; returns the max errors.
+    ``o32_gpu``: the forward's fp32 O (before its rounding to bf16), compared
+    with the oracle at the flat O tolerance, no store allowance ("o32")."""
     tol = TOL[dtype]
     Oo, Lo, Mo = O.sparse_forward(Qh, Kh, Vh, block, rp, ci, scale, rows=rows)
     B, H, N, D = Qh.shape
     nb = O.num_blocks(N, block)
     err = {"o": 0.0, "o_excess": 0.0, "lse": 0.0, "mass": 0.0}
+    if o32_gpu is not None:
+        err["o32"] = 0.0
     for r in rows:
         bh, i = divmod(r, nb)
         b, h = divmod(bh, H)
@@ -72,6 +76,8 @@ def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass
         diff = np.abs(og - oo)
         err["o"] = max(err["o"], float(diff.max()))
         err["o_excess"] = max(err["o_excess"], float((diff - tol["o"] - tol["store_rel"] * np.abs(oo)).max()))
+        if o32_gpu is not None:
+            err["o32"] = max(err["o32"], float(np.abs(o32_gpu[b, h, lo:hi].astype(np.float64) - oo).max()))
         lg, lo_ = lse_gpu[b, h, lo:hi], Lo[b, h, lo:hi]
         fin = np.isfinite(lo_)
         assert np.array_equal(np.isfinite(lg), fin), f"row {r}: -inf pattern of LSE differs"
@@ -87,16 +93,29 @@ def compare_forward(Qh, Kh, Vh, block, rp, ci, scale, rows, o_gpu, lse_gpu, mass
 def assert_forward_within(err: dict, dtype: str, what: str = ""):
     tol = TOL[dtype]
     assert err["o_excess"] <= 0.0, f"{what} O error {err['o']:.3g} beyond {tol['o']} (+ bf16 store rounding)"
+    if "o32" in err:
+        assert err["o32"] <= tol["o"], f"{what} fp32 O error {err['o32']:.3g} > {tol['o']}"
     assert err["lse"] <= tol["lse"], f"{what} LSE error {err['lse']:.3g} > {tol['lse']}"
     assert err["mass"] <= tol["mass"], f"{what} mass error {err['mass']:.3g} > {tol['mass']}"
 
 
-def sample_rows(R: int, nb: int, count: int, seed: int = 0) -> list[int]:
+def sample_rows(R: int, nb: int, count: int, seed: int = 0, row_ptr=None) -> list[int]:
     """Rows to check against the oracle: the first and last block of the first
-    and last head (ragged tail), plus a seeded random sample."""
+    and last head (ragged tail), plus a seeded random sample.  With the CSR's
+    ``row_ptr``, also every head's longest row, its shortest non-empty row and
+    one seeded random row of it."""
     rng = np.random.default_rng(seed)
     fixed = {0, nb - 1, R - nb, R - 1}
     extra = rng.choice(R, size=min(count, R), replace=False).tolist()
+    if row_ptr is not None:
+        lens = np.diff(np.asarray(row_ptr, dtype=np.int64)[:R + 1])
+        for r0 in range(0, R, nb):
+            ln = lens[r0:r0 + nb]
+            fixed.add(r0 + int(np.argmax(ln)))
+            nz = np.nonzero(ln > 0)[0]
+            if nz.size:
+                fixed.add(r0 + int(nz[np.argmin(ln[nz])]))
+            fixed.add(r0 + int(rng.integers(nb)))
     return sorted(fixed | set(extra))
 
 
@@ -129,23 +148,32 @@ def compare_backward(x, block, rp, ci, scale, heads, grads_gpu, dtype: str):
 
 def messy_rows(rng, R: int, nb: int) -> list:
     """Candidate / mask rows outside the strictly ascending form, for a grid of
-    65 <= nb <= 200 blocks (a row is then read up to 256 entries):
-      r % 4 == 0  repeats inside one 64-entry chunk (the first 10 ids twice);
-      r % 4 == 1  repeats across chunks, negative ids between the listings;
-      r % 4 == 2  ascending, 300 leading negative ids and 3 ids >= nb, so the
+    65 <= nb <= 200 blocks (the selection kernels then hold 256 block slots):
+      r % 6 == 0  repeats inside one 64-entry chunk (the first 10 ids twice);
+      r % 6 == 1  repeats across chunks, negative ids between the listings;
+      r % 6 == 2  ascending, 300 leading negative ids and 3 ids >= nb, so the
                   row is longer than 256 entries;
-      r % 4 == 3  strictly ascending."""
+      r % 6 == 3  strictly ascending;
+      r % 6 == 4  non-decreasing, every id listed 3 times (86 or more ids, so
+                  the row is longer than 256 entries);
+      r % 6 == 5  unordered: a shuffled row with repeats and bad ids mixed in."""
     assert 65 <= nb <= 200
     rows = []
     for r in range(R):
-        kind = r % 4
-        c = np.sort(rng.choice(nb, size=int(rng.integers(1, (60 if kind < 2 else nb) + 1)), replace=False))
+        kind = r % 6
+        lo, hi = (86, nb) if kind == 4 else (1, 60 if kind < 2 else nb)
+        c = np.sort(rng.choice(nb, size=int(rng.integers(lo, hi + 1)), replace=False))
         if kind == 0:
             rows.append(np.concatenate([c[:10], c[:10], c[10:]]))
         elif kind == 1:
             rows.append(np.concatenate([c, np.full(64 - c.size, -1), c]))
         elif kind == 2:
             rows.append(np.concatenate([np.arange(-300, 0), c, np.arange(nb, nb + 3)]))
+        elif kind == 4:
+            rows.append(np.repeat(c, 3))
+        elif kind == 5:
+            x = np.concatenate([c, c[: c.size // 2], [-1, nb, -7]])
+            rows.append(x[rng.permutation(x.size)])
         else:
             rows.append(c)
     return rows

@@ -8,7 +8,20 @@ import pytest
 
 from block_sparse_attention_16_amd import _lib
 
-needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbsa.so not built")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    """Builds libbsa.so when it is missing and hipcc is present (hipcc
+    cross-compiles gfx950 without a GPU), so a fresh checkout runs these tests
+    instead of skipping them."""
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_16_amd import build as B
+        try:
+            B.hipcc()
+        except RuntimeError:
+            pytest.skip("libbsa.so is not built and hipcc is not available to build it")
+        B.build(verbose=False)
 
 FAKE = 0x10000      # a 16-byte aligned address that validation never dereferences
 
@@ -23,7 +36,6 @@ def _csr(cap=1024):
     return _lib.BsaCsr(FAKE, FAKE + 4096, cap)
 
 
-@needs_lib
 def test_library_exports_every_header_function():
     names = _lib.header_functions()
     assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_estimate_mask_hierarchical", "bsa_forward",
@@ -38,7 +50,6 @@ def test_library_exports_every_header_function():
     assert set(names) <= exported
 
 
-@needs_lib
 def test_status_strings_and_version():
     L = _lib.load()
     assert L.bsa_status_string(0) == b"ok"
@@ -46,7 +57,6 @@ def test_status_strings_and_version():
     assert L.bsa_version() >= 100
 
 
-@needs_lib
 def test_workspace_sizes():
     L = _lib.load()
     s = _shape()
@@ -69,7 +79,6 @@ def _est(L, shape, q=FAKE, k=FAKE, p=0.9, scale=0.0, cand=None, keep=0, out=None
                                ctypes.byref(out), ws, ws_bytes, None)
 
 
-@needs_lib
 def test_estimate_validation():
     L = _lib.load()
     s = _shape()
@@ -98,7 +107,6 @@ def test_estimate_validation():
     assert _est(L, s, out=neg) == _lib.BSA_ERR_INVALID_ARG
 
 
-@needs_lib
 def test_hierarchical_estimate_validation():
     L = _lib.load()
     s = _shape()
@@ -114,7 +122,6 @@ def test_hierarchical_estimate_validation():
     assert call(4, p=0.0) == _lib.BSA_ERR_INVALID_ARG
 
 
-@needs_lib
 def test_forward_and_backward_validation():
     L = _lib.load()
     s = _shape()
@@ -144,7 +151,6 @@ def test_forward_and_backward_validation():
     assert st == _lib.BSA_ERR_UNSUPPORTED
 
 
-@needs_lib
 def test_select_from_mass_validation():
     L = _lib.load()
     s = _shape()
@@ -166,7 +172,6 @@ def test_select_from_mass_validation():
     assert call(shape=_shape(block=96)) == _lib.BSA_ERR_UNSUPPORTED
 
 
-@needs_lib
 def test_structured_mask_validation():
     L = _lib.load()
     s = _shape()
@@ -192,7 +197,6 @@ def test_structured_mask_validation():
     assert call(shape=_shape(D=80)) == _lib.BSA_ERR_UNSUPPORTED
 
 
-@needs_lib
 def test_permute_rows_validation():
     L = _lib.load()
 

@@ -118,8 +118,9 @@ def test_narrowing_empty_and_tiny_rows(bsa):
 
 def test_narrowing_repeated_ids_and_long_rows(bsa):
     """Rows that repeat ids (the first listing's mass counts, also when both
-    listings fall in one 64-entry chunk) or list ids outside [0, nb) (ignored,
-    also when they make the row longer than the entries a row is read up to)."""
+    listings fall in one 64-entry chunk, and in shuffled rows) or list ids
+    outside [0, nb) (ignored), including rows longer than the kernel's 256
+    block slots."""
     nb, bs, H = 100, 64, 2
     rng = np.random.default_rng(43)
     rp, ci = O.rows_to_csr(messy_rows(rng, H * nb, nb))

@@ -224,9 +224,9 @@ def test_candidate_path_and_forced_prefix(bsa, dtype):
 
 def test_candidate_rows_with_repeats_and_out_of_grid_ids(bsa):
     """Candidate rows select what their distinct ids in [0, nb) select:
-    repeats inside one 64-entry chunk and across chunks, and ascending rows
-    whose leading negative ids make them longer than the entries a row is
-    read up to."""
+    repeats inside one 64-entry chunk and across chunks, rows longer than the
+    kernel's 256 block slots (leading negative ids, or every id listed three
+    times), and shuffled rows with repeats and out-of-grid ids."""
     from tests.gpu_helpers import messy_rows
     rng = np.random.default_rng(41)
     B, H, N, D, bs = 1, 2, 100 * 64 - 5, 64, 64

@@ -51,6 +51,10 @@ MUTATIONS = [
     ("candidate_ids_unfiltered", "            cand = cand[(cand >= 0) & (cand < nb)]\n", ""),
     ("candidates_ignored", "rows.append(top_p_select(cand, logits[i, cand], top_p, forced))",
      "rows.append(top_p_select(np.arange(nb), logits[i], top_p, forced))"),
+    # estimator over whole [B, H, N, D] tensors
+    ("candidate_slice_ignores_batch", "        base = (b * H + h) * nb\n", "        base = h * nb\n"),
+    ("rows_in_h_b_order", "[(b, h) for b in range(B) for h in range(H)]",
+     "[(b, h) for h in range(H) for b in range(B)]"),
     # bands that excuse GPU/oracle differences
     ("band_value_tol_doubled", "if (r < row.k_star and s <= s_next + tol) or (r >= row.k_star and s >= s_last - tol):",
      "if (r < row.k_star and s <= s_next + 2 * tol) or (r >= row.k_star and s >= s_last - 2 * tol):"),

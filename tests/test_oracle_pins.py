@@ -178,6 +178,83 @@ def test_candidate_restriction():
     assert [r.candidates.tolist() for r in got] == [c.tolist() for c in cands]
 
 
+def _dominant_block_heads(B, H, nb, bs, D, j_star):
+    """Q, K [B, H, nb*bs, D] whose pooled logits make block j_star(b, h) take
+    all but ~1e-8 of every row's probability: every query is e_0, and the keys
+    are zero except block j_star(b, h), whose keys are 40 e_0 (logit 40 * scale
+    against 0 for every other block)."""
+    N = nb * bs
+    q = np.zeros((B, H, N, D))
+    q[..., 0] = 1.0
+    k = np.zeros((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            j = j_star(b, h)
+            k[b, h, j * bs:(j + 1) * bs, 0] = 40.0
+    return q, k
+
+
+def test_estimate_mask_rows_follow_b_h_i_order_at_b_above_1():
+    """Closed form at B = 2, H = 3: every row of head (b, h) selects exactly the
+    dominant block j*(b, h) = (3b + h) mod nb, and the CSR lists rows in
+    (b, h, i) order -- so a head order of (h, b) or a head's rows read from
+    another head shows up as a wrong block."""
+    B, H, nb, bs, D = 2, 3, 5, 16, 4
+    j_star = lambda b, h: (3 * b + h) % nb
+    q, k = _dominant_block_heads(B, H, nb, bs, D, j_star)
+    rp, ci, sels = O.estimate_mask(q, k, bs, 0.5, 0.5)
+    assert rp.tolist() == list(range(B * H * nb + 1))
+    assert ci.tolist() == [j_star(b, h) for b in range(B) for h in range(H) for _ in range(nb)]
+    assert sorted(sels) == [(b, h) for b in range(B) for h in range(H)]
+
+
+def test_estimate_mask_candidate_rows_are_taken_from_their_own_head():
+    """B = 2, H = 3 with single-block candidate rows: a row whose only candidate
+    is c keeps exactly c (k* >= 1), whatever the logits.  The candidate of row
+    r = (b*H + h)*nb + i is c(b, h, i) = (7(bH + h) + 2i) mod nb, different for
+    the two b of one h, so reading head (b, h)'s candidates from any other
+    head's rows changes the output."""
+    B, H, nb, bs, D = 2, 3, 5, 16, 4
+    rng = np.random.default_rng(61)
+    q = rng.normal(size=(B, H, nb * bs, D))
+    k = rng.normal(size=(B, H, nb * bs, D))
+    c = lambda b, h, i: (7 * (b * H + h) + 2 * i) % nb
+    want = [c(b, h, i) for b in range(B) for h in range(H) for i in range(nb)]
+    cand = (np.arange(B * H * nb + 1), np.array(want))
+    rp, ci, _ = O.estimate_mask(q, k, bs, 0.9, 0.5, candidate=cand)
+    assert rp.tolist() == list(range(B * H * nb + 1))
+    assert ci.tolist() == want
+    # with the same dominant-block inputs as above, a two-block candidate row
+    # {c, j*} keeps j* alone (probability ~1 - 1e-8 >= p), and {c} alone when
+    # c == j* -- rows again read from their own head only
+    j_star = lambda b, h: (3 * b + h) % nb
+    q2, k2 = _dominant_block_heads(B, H, nb, bs, D, j_star)
+    rows = [np.unique([c(b, h, i), j_star(b, h)]) for b in range(B) for h in range(H) for i in range(nb)]
+    rp2, ci2, _ = O.estimate_mask(q2, k2, bs, 0.5, 0.5, candidate=O.rows_to_csr(rows))
+    assert ci2.tolist() == [j_star(b, h) for b in range(B) for h in range(H) for _ in range(nb)]
+
+
+def test_estimate_mask_random_candidates_equal_per_head_rows():
+    """B = 2, H = 3, random candidate CSR: every row r = (b*H + h)*nb + i of the
+    whole-tensor estimator equals the single-head estimator run on head (b, h)
+    with that head's candidate rows, sliced out here by explicit row index."""
+    B, H, N, bs, D = 2, 3, 300, 64, 8
+    rng = np.random.default_rng(62)
+    q = rng.normal(size=(B, H, N, D))
+    k = rng.normal(size=(B, H, N, D)) + 0.5 * q
+    nb = O.num_blocks(N, bs)
+    cand_rows = [np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False))
+                 for _ in range(B * H * nb)]
+    rp, ci, _ = O.estimate_mask(q, k, bs, 0.7, 0.3, candidate=O.rows_to_csr(cand_rows), keep_prefix_tokens=5)
+    for b in range(B):
+        for h in range(H):
+            mine = [cand_rows[(b * H + h) * nb + i] for i in range(nb)]
+            ref = O.estimate_head(q[b, h], k[b, h], bs, 0.7, 0.3, mine, keep_prefix_tokens=5)
+            for i in range(nb):
+                r = (b * H + h) * nb + i
+                assert ci[rp[r]:rp[r + 1]].tolist() == ref[i].selected.tolist(), (b, h, i)
+
+
 # ----------------------------------------------------------------------------
 # pooling
 # ----------------------------------------------------------------------------
