@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     L.bsa_estimate_mask_hierarchical.restype = i32
     L.bsa_select_from_mass.argtypes = [P(BsaShape), P(BsaCsr), vp, f32, i32, P(BsaCsr), vp, sz, vp]
     L.bsa_select_from_mass.restype = i32
+    L.bsa_select_from_mass_noalloc.argtypes = [P(BsaShape), P(BsaCsr), vp, f32, i32, P(BsaCsr), vp]
+    L.bsa_select_from_mass_noalloc.restype = i32
     L.bsa_structured_mask.argtypes = [P(BsaShape), vp, P(BsaPatternParams), P(BsaCsr), vp, sz, vp]
     L.bsa_structured_mask.restype = i32
     L.bsa_permute_rows.argtypes = [i64, i32, i32, vp, vp, i32, vp, vp]

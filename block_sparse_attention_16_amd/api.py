@@ -189,6 +189,30 @@ def bsa_select_from_mass(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: 
     return out
 
 
+def bsa_select_from_mass_noalloc(q: torch.Tensor, mask: Csr, mass: torch.Tensor, top_p: float, block: int,
+                                 keep_prefix_tokens: int = 0, out: Csr | None = None) -> Csr:
+    """Mask narrowing without a workspace (bsa_select_from_mass_noalloc in
+    include/bsa.h): the library's per-GPU static scratch replaces the
+    workspace; ``out`` should be preallocated by callers that cannot allocate."""
+    _check(q, "q")
+    _check(mass, "mass", dtype=torch.float32, device=q.device)
+    if mass.numel() < mask.capacity:
+        raise ValueError("mass must hold mask.capacity entries")
+    shape = _shape_of(q, block)
+    nb = -(-q.shape[2] // block)
+    R = num_rows(q, block)
+    if out is None:
+        out = Csr(torch.empty(R + 1, dtype=torch.int32, device=q.device),
+                  torch.empty(R * nb, dtype=torch.int32, device=q.device))
+    _check_csr(mask, R, "mask", q.device)
+    _check_csr(out, R, "out", q.device)
+    mc, oc = mask.c(), out.c()
+    st = load().bsa_select_from_mass_noalloc(ctypes.byref(shape), ctypes.byref(mc), mass.data_ptr(), float(top_p),
+                                             int(keep_prefix_tokens), ctypes.byref(oc), _stream())
+    check(st, "bsa_select_from_mass_noalloc")
+    return out
+
+
 def bsa_structured_mask(q: torch.Tensor, head_kind: torch.Tensor, block: int, prefix_tokens: int = 0,
                         frame_tokens: int = 1, band: int = 0, period: int = 1, stripes: torch.Tensor | None = None,
                         out: Csr | None = None, workspace: torch.Tensor | None = None) -> Csr:

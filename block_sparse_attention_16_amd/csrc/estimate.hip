@@ -40,6 +40,8 @@
 // lane, into the same bitmask, then the same csr_kernel.
 #include "bsa_internal.h"
 
+#include <mutex>
+
 namespace bsa {
 namespace {
 
@@ -782,6 +784,39 @@ hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const 
   launch_select_any<true>(p, mass, top_p, mask, n_forced, w.counts, w.bits, w.words, s);
   launch_csr(p, w.counts, w.bits, w.words, out, s);
   return hipGetLastError();
+}
+
+// ---- narrowing without a caller workspace ----
+// Device-resident scratch for the narrowing kernels' counts and bitmask, for
+// callers that cannot allocate device memory.  One copy per GPU, held until
+// the process ends; every call on a GPU shares it, so calls that overlap on
+// one GPU race.  Both kernels overwrite what they use (every row's count and
+// every bitmask word), so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // The array's host-side name is only a stand-in: its device address is
+    // looked up once per device, with that device current.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, const bsa_pattern_params& prm,

@@ -164,6 +164,20 @@ bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, con
                                 float top_p, int32_t keep_prefix_tokens, bsa_csr* out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* bsa_select_from_mass without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * bsa_select_from_mass, except that the kernels' scratch (R row counts and
+ * an R x ceil(nb/32) word bitmask, 4 bytes each) lives in a 16 MiB array
+ * that the library holds on each GPU until the process ends; a shape that
+ * needs more returns BSA_ERR_WORKSPACE.  Every call on one GPU shares that
+ * array, so calls that overlap on one GPU (e.g. on two streams) race; calls
+ * in one stream are safe.  The first call on a device looks the array's
+ * device address up (a HIP failure there returns BSA_ERR_HIP).  Allocates
+ * nothing. */
+bsa_status bsa_select_from_mass_noalloc(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass,
+                                        float top_p, int32_t keep_prefix_tokens, bsa_csr* out, void* stream);
+
 /* Structured (static) head patterns.  The SVG page (Abstract) sorts heads
  * into spatial heads, where tokens of the same frame dominate, and temporal
  * heads, where tokens at the same position in other frames dominate; the

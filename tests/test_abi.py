@@ -40,7 +40,8 @@ def test_library_exports_every_header_function():
     names = _lib.header_functions()
     assert names == sorted(["bsa_backward", "bsa_estimate_mask", "bsa_estimate_mask_hierarchical", "bsa_forward",
                             "bsa_last_error",
-                            "bsa_permute_rows", "bsa_select_from_mass", "bsa_status_string", "bsa_structured_mask", "bsa_version",
+                            "bsa_permute_rows", "bsa_select_from_mass", "bsa_select_from_mass_noalloc", "bsa_status_string",
+                            "bsa_structured_mask", "bsa_version",
                             "bsa_workspace_size"])
     L = _lib.load()
     for n in names:
@@ -170,6 +171,31 @@ def test_select_from_mass_validation():
     assert call(out=m) == _lib.BSA_ERR_INVALID_ARG                     # mask aliases out
     assert call(ws_bytes=8) == _lib.BSA_ERR_WORKSPACE
     assert call(shape=_shape(block=96)) == _lib.BSA_ERR_UNSUPPORTED
+
+
+def test_select_from_mass_noalloc_validation():
+    """Host checks of the no-allocation narrowing, before any device call:
+    the same argument errors as bsa_select_from_mass, and a shape whose
+    counts and bitmask exceed the built-in 16 MiB scratch is refused."""
+    L = _lib.load()
+    s = _shape()
+    m, o = _csr(), _lib.BsaCsr(FAKE + 8192, FAKE + 16384, 1024)
+
+    def call(shape=s, mask=m, mass=FAKE, p=0.9, keep=0, out=o):
+        return L.bsa_select_from_mass_noalloc(ctypes.byref(shape), ctypes.byref(mask) if mask else None, mass, p,
+                                              keep, ctypes.byref(out) if out else None, None)
+
+    assert call(mass=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(mask=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(out=None) == _lib.BSA_ERR_INVALID_ARG
+    assert call(p=0.0) == _lib.BSA_ERR_INVALID_ARG
+    assert call(keep=-3) == _lib.BSA_ERR_INVALID_ARG
+    assert call(out=m) == _lib.BSA_ERR_INVALID_ARG                     # mask aliases out
+    assert call(shape=_shape(block=96)) == _lib.BSA_ERR_UNSUPPORTED
+    # 4096 blocks per head, 64 heads: 262,144 rows x (1 + 128) words x 4 bytes > 16 MiB
+    big = _shape(B=1, H=64, N=4096 * 64, D=64, block=64)
+    assert call(shape=big) == _lib.BSA_ERR_WORKSPACE
+    assert b"scratch" in L.bsa_last_error()
 
 
 def test_structured_mask_validation():
