@@ -138,19 +138,26 @@ bsa_status bsa_estimate_mask_hierarchical(const bsa_shape* shape, const void* q,
                          stream, kMaxSubBlocks);
 }
 
-bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass, float top_p,
-                                int32_t keep_prefix_tokens, bsa_csr* out, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  bsa::Problem p;
-  BSA_TRY(make_problem(shape, &p));
+// Argument checks shared by the two narrowing entry points.
+static bsa_status check_select_args(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass,
+                                    float top_p, int32_t keep_prefix_tokens, const bsa_csr* out, bsa::Problem* p) {
+  BSA_TRY(make_problem(shape, p));
   BSA_TRY(check_csr(mask, "mask"));
   BSA_TRY(check_csr(out, "out"));
   if (mask->capacity > 0 && !block_mass) return fail(BSA_ERR_INVALID_ARG, "block_mass is NULL");
   if (!(top_p > 0.f && top_p <= 1.f)) return fail(BSA_ERR_INVALID_ARG, "top_p=%g is outside (0, 1]", top_p);
-  if (keep_prefix_tokens < 0 || keep_prefix_tokens > p.N)
+  if (keep_prefix_tokens < 0 || keep_prefix_tokens > p->N)
     return fail(BSA_ERR_INVALID_ARG, "keep_prefix_tokens=%d is outside [0, N]", keep_prefix_tokens);
   if (mask->row_ptr == out->row_ptr || (mask->col_idx && mask->col_idx == out->col_idx))
     return fail(BSA_ERR_INVALID_ARG, "mask aliases out");
+  return BSA_OK;
+}
+
+bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass, float top_p,
+                                int32_t keep_prefix_tokens, bsa_csr* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  bsa::Problem p;
+  BSA_TRY(check_select_args(shape, mask, block_mass, top_p, keep_prefix_tokens, out, &p));
   size_t need = 0;
   bsa::carve_select(p, nullptr, &need);
   if (ws_bytes < need || (need && !ws))
@@ -165,22 +172,14 @@ bsa_status bsa_select_from_mass_noalloc(const bsa_shape* shape, const bsa_csr* m
                                         float top_p, int32_t keep_prefix_tokens, bsa_csr* out, void* stream) {
   g_err[0] = 0;
   bsa::Problem p;
-  BSA_TRY(make_problem(shape, &p));
-  BSA_TRY(check_csr(mask, "mask"));
-  BSA_TRY(check_csr(out, "out"));
-  if (mask->capacity > 0 && !block_mass) return fail(BSA_ERR_INVALID_ARG, "block_mass is NULL");
-  if (!(top_p > 0.f && top_p <= 1.f)) return fail(BSA_ERR_INVALID_ARG, "top_p=%g is outside (0, 1]", top_p);
-  if (keep_prefix_tokens < 0 || keep_prefix_tokens > p.N)
-    return fail(BSA_ERR_INVALID_ARG, "keep_prefix_tokens=%d is outside [0, N]", keep_prefix_tokens);
-  if (mask->row_ptr == out->row_ptr || (mask->col_idx && mask->col_idx == out->col_idx))
-    return fail(BSA_ERR_INVALID_ARG, "mask aliases out");
+  BSA_TRY(check_select_args(shape, mask, block_mass, top_p, keep_prefix_tokens, out, &p));
   size_t need = 0;
   bsa::carve_select(p, nullptr, &need);
   if (need > bsa::kNoAllocScratchBytes)
     return fail(BSA_ERR_WORKSPACE, "narrowing needs %zu bytes of scratch; the built-in scratch holds %zu",
                 need, bsa::kNoAllocScratchBytes);
   void* scratch = nullptr;
-  BSA_TRY(hip_status(bsa::scratch_for_current_device(&scratch), "scratch lookup"));
+  BSA_TRY(hip_status(bsa::scratch_for_stream(static_cast<hipStream_t>(stream), &scratch), "scratch lookup"));
   bsa::SelectWs w = bsa::carve_select(p, scratch, &need);
   return hip_status(bsa::launch_select_from_mass(p, mask, block_mass, top_p, keep_prefix_tokens, out, w,
                                                  static_cast<hipStream_t>(stream)),

@@ -57,9 +57,10 @@ SelectWs carve_select(const Problem& p, void* ws, size_t* bytes);
 hipError_t launch_select_from_mass(const Problem& p, const bsa_csr* mask, const float* mass, float top_p,
                                    int keep_prefix_tokens, const bsa_csr* out, const SelectWs& w, hipStream_t s);
 // Narrowing without a caller workspace: the device address of the library's
-// static scratch array on the current device (looked up once per device).
+// static scratch array on the stream's device (the current device for the
+// null stream), looked up once per device.
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;   // 16 MiB per GPU
-hipError_t scratch_for_current_device(void** ptr);
+hipError_t scratch_for_stream(hipStream_t stream, void** ptr);
 
 // ---- structured head masks (estimate.hip); same workspace as narrowing ----
 hipError_t launch_structured_mask(const Problem& p, const int32_t* head_kind, const bsa_pattern_params& prm,

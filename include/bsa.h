@@ -172,9 +172,11 @@ bsa_status bsa_select_from_mass(const bsa_shape* shape, const bsa_csr* mask, con
  * that the library holds on each GPU until the process ends; a shape that
  * needs more returns BSA_ERR_WORKSPACE.  Every call on one GPU shares that
  * array, so calls that overlap on one GPU (e.g. on two streams) race; calls
- * in one stream are safe.  The first call on a device looks the array's
- * device address up (a HIP failure there returns BSA_ERR_HIP).  Allocates
- * nothing. */
+ * in one stream are safe.  The array used is that of the stream's device
+ * (the current device for the NULL stream); the first call on a device
+ * looks its address up, making that device current for the lookup and
+ * restoring the caller's current device (a HIP failure there returns
+ * BSA_ERR_HIP).  Allocates nothing. */
 bsa_status bsa_select_from_mass_noalloc(const bsa_shape* shape, const bsa_csr* mask, const float* block_mass,
                                         float top_p, int32_t keep_prefix_tokens, bsa_csr* out, void* stream);
 
