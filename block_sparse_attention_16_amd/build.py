@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libbsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["bsa_api.cpp", "estimate.hip", "forward_bf16.hip", "forward_fp32.hip", "backward.hip",
-           "backward_fp32.hip", "permute.hip", "order.hip"]
+           "backward_fp32.hip", "permute.hip", "order.hip", "scratch.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
