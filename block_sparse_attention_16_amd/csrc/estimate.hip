@@ -46,6 +46,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSortMax = 4096;   // largest candidate row (nb <= 4096)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 template <class T>
 struct Load8;
@@ -151,13 +152,36 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// Lane exchange through DPP (a VALU move from another lane of the same row).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+// Max and sum over aligned groups of GS consecutive lanes (GS = 2, 4, 8):
+// DPP quad permutes for lanes ^ 1 and ^ 2, ds_bpermute for ^ 4.
+template <int GS>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __uint_as_float(dpp<0xB1>(__float_as_uint(x))));       // quad_perm [1,0,3,2]
+  if constexpr (GS >= 4) x = fmaxf(x, __uint_as_float(dpp<0x4E>(__float_as_uint(x))));   // [2,3,0,1]
+  if constexpr (GS >= 8) x = fmaxf(x, __shfl_xor(x, 4));
+  return x;
+}
+template <int GS>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __uint_as_float(dpp<0xB1>(__float_as_uint(x)));
+  if constexpr (GS >= 4) x += __uint_as_float(dpp<0x4E>(__float_as_uint(x)));
+  if constexpr (GS >= 8) x += __shfl_xor(x, 4);
+  return x;
+}
+
 // Pooled logits L[bh, i, j] = scale * <Qbar_i, Kbar_j> for one 64 x 64 tile
 // of one head on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32
 // products, fp32 accumulation, twice the rate of the vector FMA path).  256
 // threads; wave w computes the 32 x 32 sub-tile (w / 2, w % 2), d summed in
 // ascending pairs.  With GS > 1 the 64 columns are key sub-blocks (GS per
 // block) and the epilogue writes each block's logit as the natural
-// log-sum-exp of its non-empty sub-blocks' logits (GS consecutive lanes).
+// log-sum-exp of its non-empty sub-blocks' logits (GS consecutive lanes;
+// max and sum by lane exchanges, exp2 / log2 on the transcendental unit).
 // grid (ceil(nb * GS / 64), ceil(nb / 64), heads from bh0).
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 template <int D, int GS>
@@ -220,14 +244,12 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float x = live ? acc[v] * scale : -INFINITY;
-      float mx = x;
-#pragma unroll
-      for (int off = 1; off < GS; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      float e = live ? expf(x - mx) : 0.f;
-#pragma unroll
-      for (int off = 1; off < GS; off <<= 1) e += __shfl_xor(e, off);
+      // a written block (jb < nb) has a token in sub-block 0: mx finite, e >= 1
+      const float mx = group_max<GS>(x);
+      const float e = group_sum<GS>(live ? __builtin_amdgcn_exp2f((x - mx) * kLog2e) : 0.f);
       const int i = i0 + wi + 8 * (v >> 2) + 4 * hi + (v & 3);
-      if (ms == 0 && i < nb && jb < nb) logits[((size_t)bh * nb + i) * nb + jb] = mx + logf(e);
+      if (ms == 0 && i < nb && jb < nb)
+        logits[((size_t)bh * nb + i) * nb + jb] = mx + __builtin_amdgcn_logf(e) * kLn2;
     }
   }
 }
@@ -238,10 +260,6 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const float* __restric
 // Each step combines a lane's value with its partner's; partners hold the
 // same two operands, so with a commutative op every lane ends with the
 // bitwise-same result (no LDS traffic, unlike ds_bpermute shuffles).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
 template <class Op>
 __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
   x = op(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
