@@ -456,9 +456,13 @@ def main(argv=None) -> int:
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / a.steps
-    est_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _, _ in ev]))
-    fwd_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2, _ in ev]))
-    bwd_ms = float(np.mean([e2.elapsed_time(e3) for _, _, e2, e3 in ev])) if w.backward else None
+    # per-step event times; means feed the roofline (comparable with rocprofv3's
+    # average duration), medians are reported beside them
+    est_t = [e0.elapsed_time(e1) for e0, e1, _, _ in ev]
+    fwd_t = [e1.elapsed_time(e2) for _, e1, e2, _ in ev]
+    bwd_t = [e2.elapsed_time(e3) for _, _, e2, e3 in ev] if w.backward else None
+    est_ms, fwd_ms = float(np.mean(est_t)), float(np.mean(fwd_t))
+    bwd_ms = float(np.mean(bwd_t)) if w.backward else None
 
     if a.copy_calibration > 0:
         src = torch.empty(a.copy_calibration // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -590,10 +594,12 @@ def main(argv=None) -> int:
         "executed_tflop_per_step": exec_flop / 1e12,
         "dense_equiv_tflop_per_step": dense_flop / 1e12,
         "dense_equiv_tflops": round(dense_flop * (3.5 if w.backward else 1.0) / (ms * 1e-3) / 1e12, 3),
-        "fwd_kernel": {"ms": round(fwd_ms, 4), "executed_tflops": round(fwd_tflops, 3),
+        "fwd_kernel": {"ms": round(fwd_ms, 4), "ms_median": round(float(np.median(fwd_t)), 4),
+                       "executed_tflops": round(fwd_tflops, 3),
                        "dense_equiv_tflops": round(dense_flop / (fwd_ms * 1e-3) / 1e12, 3),
                        "pct_bf16_peak": round(100 * fwd_tflops / BF16_PEAK_TFLOPS, 2)},
-        "estimator": {"ms": round(est_ms, 4), "algorithmic_bytes": est_bytes,
+        "estimator": {"ms": round(est_ms, 4), "ms_median": round(float(np.median(est_t)), 4),
+                      "algorithmic_bytes": est_bytes,
                       "gbps": round(est_bytes / (est_ms * 1e-3) / 1e9, 1),
                       "pct_hbm_peak": round(100 * est_bytes / (est_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                       "counted_bytes": est_counted,
@@ -623,6 +629,7 @@ def main(argv=None) -> int:
                               "block_density": struct_nnz / (R * w.nb)}
     if w.backward:
         out["bwd_ms"] = round(bwd_ms, 4)
+        out["bwd_ms_median"] = round(float(np.median(bwd_t)), 4)
         out["bwd_executed_tflops"] = round(2.5 * exec_flop / (bwd_ms * 1e-3) / 1e12, 3)
     if not a.no_gsrs_loop:
         print("bench: reduced-search loop over the Wan2.1-like steps", file=sys.stderr, flush=True)
