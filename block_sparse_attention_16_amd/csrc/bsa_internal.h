@@ -92,6 +92,8 @@ void launch_tail_order(const int32_t* row_ptr, int64_t cap, const int32_t* count
 struct ForwardWs {
   float* part;       // [capacity, bs] per-entry, per-query block log-sum-exp (block mass)
   int32_t* order;    // [tail_rows(R)] rows of the grid's tail, longest first
+  uint32_t* units;   // bf16, block 64: [capacity] unit lists of the pair grid
+  int32_t* ulen;     // bf16, block 64: [B*H*ceil(nb/2)] their lengths
 };
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes);
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,

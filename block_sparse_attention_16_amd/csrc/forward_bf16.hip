@@ -8,7 +8,9 @@
 //
 // Workgroup = one mask row (query block i of head bh), BS/32 waves.  Wave w
 // owns queries [32w, 32w + 32) of the block and every key of each visited key
-// block, with its own online-softmax state.  Two waves share each SIMD.
+// block, with its own online-softmax state.  Two waves share each SIMD.  With
+// 64-token blocks a workgroup takes two adjacent mask rows instead (the pair
+// grid, PAIR below), so that every workgroup has 128 queries and 64-key units.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = K rows from LDS, B = Q^T held in registers.  In the 32x32 accumulator a
@@ -326,13 +328,25 @@ __device__ __forceinline__ void phase_c(const char* vs, const bf16x8 (&pb)[C::KC
 
 // WRITE_O32: also store O in fp32 (a separate instantiation, so that the
 // common kernel is compiled without the extra epilogue).
-template <int BS, int D, bool WRITE_O32>
+// PAIR (64-token blocks): a 128-query workgroup takes the two mask rows of
+// query blocks 2m and 2m + 1 of a head (waves 0-1 and 2-3), walking the unit
+// list built by pair_units_kernel: one 64-key block per unit, with flags for
+// the rows that list it.  Every unit's K/V tiles are copied once for both
+// rows; a wave scores a unit its row does not list as -inf throughout, which
+// adds exact zeros, so each row's results are those of a walk over its own
+// list.  On the video training masks adjacent rows share ~89 % of their
+// blocks.
+template <int BS, int D, bool WRITE_O32, bool PAIR = false>
 __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two waves per SIMD
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap, __bf16* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ mass, float* __restrict__ part, float* __restrict__ o32, int N,
-    int nb, float scale, const int32_t* __restrict__ order, int t0) {
+    int nb, float scale, const int32_t* __restrict__ order, int t0, const uint32_t* __restrict__ units,
+    const int32_t* __restrict__ ulen) {
   using C = Cfg<BS, D>;
+  static_assert(!PAIR || BS == 128, "a pair of 64-token query blocks fills a 128-query workgroup");
+  constexpr int KB = PAIR ? 64 : BS;          // tokens per key block and per mask row's query block
+  constexpr int UPE = PAIR ? 1 : C::U;        // units per listed key block
   // LDS tiles.  Distinct objects, each used at a fixed place of the loop, let
   // the compiler see that reads of one tile do not wait on the DMA into another.
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
@@ -347,7 +361,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   // Head-major up to t0, so that rows running together share K/V in the
   // caches; the last rows of the grid longest first (order).
   const int r = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
-  const int bh = r / nb, i = r - bh * nb;
+  const int nbw = PAIR ? (nb + 1) / 2 : nb;  // workgroup rows per head
+  const int bh = r / nbw, i = r - bh * nbw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int l32 = lane & 31, hf = lane >> 5;
@@ -356,10 +371,18 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   const int qloc = wave * 32 + l32;          // this lane's query within the block
   const int qq = q0 + qloc;
 
-  int64_t e_begin = row_ptr[r], e_end = row_ptr[r + 1];
-  if (e_end > cap) e_end = cap;
-  if (e_begin < 0) e_begin = 0;
-  if (e_begin > e_end) e_begin = e_end;
+  // This wave's mask row: the workgroup's row, or in a pair row 2i (waves
+  // 0-1) or 2i + 1 (waves 2-3, absent when 2i + 1 = nb).
+  const int wrow = PAIR ? (wave >> 1) : 0;
+  const int64_t rrow = PAIR ? (int64_t)bh * nb + 2 * i + wrow : r;
+  int64_t e_begin = 0, e_end = 0;
+  if (!PAIR || 2 * i + wrow < nb) {
+    e_begin = row_ptr[rrow];
+    e_end = row_ptr[rrow + 1];
+    if (e_end > cap) e_end = cap;
+    if (e_begin < 0) e_begin = 0;
+    if (e_begin > e_end) e_begin = e_end;
+  }
   const int n_e = (int)(e_end - e_begin);
 
   const auto kh = head_rsrc(k + (size_t)bh * N * D, N, D);
@@ -397,17 +420,34 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   // entries' key-block ids with vector buffer loads one iteration ahead (so
   // they land under the same wait as the tile DMAs, and ids past the row read
   // as 0 without a bounds test); the prologue reads its first ids directly.
-  const int n_u = n_e * C::U;
-  const auto colr = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col_idx + e_begin), (short)0, n_e * 4,
+  // Ids of the units: the row's CSR entries, or the pair's unit list (which
+  // starts where row 2i's entries start).
+  const int32_t* ids = col_idx + e_begin;
+  int n_u = n_e * UPE;
+  if constexpr (PAIR) {
+    int64_t a = row_ptr[(int64_t)bh * nb + 2 * i];
+    a = a < 0 ? 0 : (a > cap ? cap : a);
+    ids = reinterpret_cast<const int32_t*>(units) + a;
+    n_u = ulen[r];
+  }
+  const auto colr = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ids), (short)0, (n_u / UPE) * 4,
                                                       0x00020000);
-  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / C::U) * 4, 0, 0); };
-  auto unit_key = [&](int j_raw, int u, int& nvk) {   // first key of unit u; nvk = its valid keys
+  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / UPE) * 4, 0, 0); };
+  // first key of unit u; nvk = its valid keys for this wave (0 for a unit
+  // that this wave's row does not list)
+  auto unit_key = [&](int j_raw, int u, int& nvk) {
+    bool mine = true;
+    if constexpr (PAIR) {
+      mine = (((uint32_t)j_raw >> (30 + wrow)) & 1u) != 0u;
+      j_raw &= 0x3fffffff;
+    }
     const bool valid = j_raw >= 0 && j_raw < nb;
-    const int key0 = (valid ? j_raw : 0) * BS + (u % C::U) * C::SUB;
-    nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
+    const int key0 = (valid ? j_raw : 0) * KB + (u % UPE) * C::SUB;
+    nvk = valid && mine ? max(0, min(C::SUB, N - key0)) : 0;
     return key0;
   };
-  auto unit_src = [&](int u, int& nvk) { return unit_key(col_idx[e_begin + u / C::U], u, nvk); };
+  auto unit_mine = [&](int j_raw) { return !PAIR || ((((uint32_t)j_raw >> (30 + wrow)) & 1u) != 0u); };
+  auto unit_src = [&](int u, int& nvk) { return unit_key(ids[u / UPE], u, nvk); };
   uint32_t koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
   for (int it = 0; it < C::LOADS; ++it) {
@@ -467,6 +507,8 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
 
   floatx16 sa[C::KC], sb[C::KC];     // scores of the current and the next unit
   int jv1 = col_load(1), jv2 = col_load(2);   // key-block ids of units u+1, u+2 (VGPR, uniform)
+  bool mine_u = n_u > 0 && unit_mine(ids[0]);  // PAIR: this wave's row lists the current unit
+  int k_row = 0;                               // PAIR: entries of this wave's row walked so far
   if (n_u > 0) {
     int nv0;
     const int key0 = unit_src(0, nv0);
@@ -494,7 +536,10 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     __syncthreads();                      // ... and every other wave's; slots of K[u], V[u-1] are free
     const bool has_next = u + 1 < n_u;
     int nvn, nn;
-    const int key1 = unit_key(__builtin_amdgcn_readfirstlane(jv1), u + 1, nvn);
+    const int jr1 = __builtin_amdgcn_readfirstlane(jv1);
+    const int key1 = unit_key(jr1, u + 1, nvn);
+    const bool mine_cur = mine_u;
+    mine_u = unit_mine(jr1);
     const int key2 = unit_key(__builtin_amdgcn_readfirstlane(jv2), u + 2, nn);
     if (u + 2 < n_u) dma_tile<BS, D>(kh, key2, k_free, wave, koff);
     if (has_next) dma_tile<BS, D>(vh, key1, v_free, wave, voff);
@@ -514,9 +559,16 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
     l_run += ls;
     lt_run += lt;
     ls_blk += ls;
-    if (u % C::U == C::U - 1) {         // last unit of the entry
-      const int it = u / C::U;
-      if (part != nullptr) {
+    if (u % UPE == UPE - 1) {           // last unit of the entry
+      if constexpr (PAIR) {
+        if (part != nullptr && mine_cur) {
+          const float lb = kHalfSums ? xhalf_sum(ls_blk) : ls_blk;
+          if (hf == 0)
+            part[(e_begin + k_row) * KB + (qloc & 63)] = lb > 0.f ? m_run + __builtin_amdgcn_logf(lb) : -INFINITY;
+        }
+        k_row += mine_cur ? 1 : 0;
+      } else if (part != nullptr) {
+        const int it = u / C::U;
         const float lb = kHalfSums ? xhalf_sum(ls_blk) : ls_blk;
         if (hf == 0) part[(e_begin + it) * BS + qloc] = lb > 0.f ? m_run + __builtin_amdgcn_logf(lb) : -INFINITY;
       }
@@ -571,11 +623,23 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
                           acc[dt][g * 4 + 3] * inv);
     }
   }
-  if (mass == nullptr || n_e == 0) return;
+  if (mass == nullptr || (!PAIR && n_e == 0)) return;   // uniform over the workgroup
   __syncthreads();
 
   // ---- exact block mass: mean over valid queries of exp2(part - lse2) ----
-  if constexpr (D == 128 && BS == 128) {
+  if constexpr (PAIR) {
+    // each row's entries by its two waves; n_e = 0 for an absent row
+    const int qr = 64 * wrow;                  // the row's first query in the workgroup
+    const int nq_row = max(0, min(64, N - (q0 + qr)));
+    for (int it = wave & 1; it < n_e; it += 2) {
+      const int64_t e = e_begin + it;
+      const int j_raw = col_idx[e];
+      float s = 0.f;
+      if (j_raw >= 0 && j_raw < nb && lane < nq_row) s = __builtin_amdgcn_exp2f(part[e * KB + lane] - lse2_s[qr + lane]);
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) mass[e] = s / (float)nq_row;
+    }
+  } else if constexpr (D == 128 && BS == 128) {
     // Four entries per wavefront at a time, 16 lanes each: lane c of a group
     // sums queries [QPL c, QPL c + QPL) (16-byte loads of part and lse2),
     // then four xor-shuffles within the group.  (Measured slower elsewhere:
@@ -624,6 +688,123 @@ __global__ __launch_bounds__(2 * BS, 2) void fwd_kernel(   // Cfg::THREADS; two 
   }
 }
 
+// Unit lists of the pair grid (fwd_kernel, PAIR): pair p is query blocks 2m
+// and 2m + 1 of head bh (rows A and B).  When both rows list strictly
+// ascending ids in [0, nb), the pair walks their union in ascending order,
+// bit 30 marking a block of A and bit 31 one of B; otherwise A's entries then
+// B's, as listed (ids outside [0, nb) kept outside).  Pair p's list goes over
+// the pair's own entries [row_ptr[A], row_ptr[B + 1]) of the unit array,
+// which hold |A| + |B| slots, at least its length; a pair whose rows are not
+// adjacent in col_idx (a decreasing row_ptr) gets no units.  One wavefront per
+// pair, the union through two LDS bitmasks.
+constexpr uint32_t kUnitA = 1u << 30, kUnitB = 1u << 31, kUnitNone = kUnitA - 1u;
+constexpr int kPairWaves = 4;
+__global__ __launch_bounds__(64 * kPairWaves) void pair_units_kernel(const int32_t* __restrict__ row_ptr,
+                                                                     const int32_t* __restrict__ col_idx,
+                                                                     int64_t cap, int nb, int P,
+                                                                     uint32_t* __restrict__ units,
+                                                                     int32_t* __restrict__ ulen) {
+  __shared__ uint32_t bits[kPairWaves][2][4096 / 32];   // nb <= 4096
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int p = blockIdx.x * kPairWaves + wid;
+  if (p >= P) return;                        // whole wavefront leaves together
+  const int np = (nb + 1) / 2;
+  const int bh = p / np, m = p - bh * np;
+  const int64_t rA = (int64_t)bh * nb + 2 * m;
+  const bool hasB = 2 * m + 1 < nb;
+  auto clampc = [&](int64_t x) { return x < 0 ? (int64_t)0 : (x > cap ? cap : x); };
+  const int64_t sA = clampc(row_ptr[rA]);
+  int64_t eA = clampc(row_ptr[rA + 1]);
+  if (eA < sA) eA = sA;
+  int64_t sB = eA, eB = eA;
+  if (hasB) {
+    sB = clampc(row_ptr[rA + 1]);
+    eB = clampc(row_ptr[rA + 2]);
+    if (eB < sB) eB = sB;
+  }
+  if (sB != eA) {
+    if (lane == 0) ulen[p] = 0;
+    return;
+  }
+  constexpr int64_t kRowMax = 1 << 30;       // entries read per row (the sum stays an int)
+  const int64_t nA = min(eA - sA, kRowMax), nB = min(eB - sB, kRowMax);
+  bool bad = false;
+  for (int64_t t = lane; t < nA; t += 64) {
+    const int x = col_idx[sA + t];
+    bad = bad || x < 0 || x >= nb || (t > 0 && col_idx[sA + t - 1] >= x);
+  }
+  for (int64_t t = lane; t < nB; t += 64) {
+    const int x = col_idx[sB + t];
+    bad = bad || x < 0 || x >= nb || (t > 0 && col_idx[sB + t - 1] >= x);
+  }
+  if (!__any(bad)) {
+    uint32_t* ba = bits[wid][0];
+    uint32_t* bb = bits[wid][1];
+    const int words = (nb + 31) / 32;
+    for (int w = lane; w < words; w += 64) {
+      ba[w] = 0u;
+      bb[w] = 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int64_t t = lane; t < nA; t += 64) {
+      const int x = col_idx[sA + t];
+      atomicOr(&ba[x >> 5], 1u << (x & 31));
+    }
+    for (int64_t t = lane; t < nB; t += 64) {
+      const int x = col_idx[sB + t];
+      atomicOr(&bb[x >> 5], 1u << (x & 31));
+    }
+    __builtin_amdgcn_wave_barrier();
+    int64_t out = sA;
+    for (int c = 0; c < (nb + 63) / 64; ++c) {
+      const int j = 64 * c + lane;
+      const bool inA = j < nb && ((ba[j >> 5] >> (j & 31)) & 1u);
+      const bool inB = j < nb && ((bb[j >> 5] >> (j & 31)) & 1u);
+      const uint64_t mk = __ballot(inA || inB);
+      if (inA || inB) {
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        units[out + rank] = (uint32_t)j | (inA ? kUnitA : 0u) | (inB ? kUnitB : 0u);
+      }
+      out += __popcll(mk);
+    }
+    if (lane == 0) ulen[p] = (int)(out - sA);
+  } else {
+    for (int64_t t = lane; t < nA; t += 64) {
+      const int x = col_idx[sA + t];
+      units[sA + t] = (x >= 0 && x < nb ? (uint32_t)x : kUnitNone) | kUnitA;
+    }
+    for (int64_t t = lane; t < nB; t += 64) {
+      const int x = col_idx[sB + t];
+      units[sA + nA + t] = (x >= 0 && x < nb ? (uint32_t)x : kUnitNone) | kUnitB;
+    }
+    if (lane == 0) ulen[p] = (int)(nA + nB);
+  }
+}
+
+// 64-token blocks: pairs of query blocks in 128-query workgroups.
+template <int D>
+hipError_t launch_pairs(const Problem& p, const void* q, const void* k, const void* v, float scale,
+                        const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
+                        hipStream_t s) {
+  using C = Cfg<128, D>;
+  const int P = p.B * p.H * ((p.nb + 1) / 2);
+  pair_units_kernel<<<(P + kPairWaves - 1) / kPairWaves, 64 * kPairWaves, 0, s>>>(
+      mask->row_ptr, mask->col_idx, mask->capacity, p.nb, P, w.units, w.ulen);
+  const int T = tail_rows(P), t0 = P - T;
+  launch_tail_order(nullptr, 0, w.ulen, t0, T, w.order, s);
+  if (o32 != nullptr)
+    fwd_kernel<128, D, true, true><<<P, C::THREADS, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
+        mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
+        scale, w.order, t0, w.units, w.ulen);
+  else
+    fwd_kernel<128, D, false, true><<<P, C::THREADS, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
+        mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, nullptr, p.N,
+        p.nb, scale, w.order, t0, w.units, w.ulen);
+  return hipGetLastError();
+}
+
 template <int BS, int D>
 hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const void* v, float scale,
                        const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
@@ -635,12 +816,12 @@ hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const voi
     fwd_kernel<BS, D, true><<<p.R, C::THREADS, 0, s>>>(
         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
         mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, o32, p.N, p.nb,
-        scale, w.order, t0);
+        scale, w.order, t0, nullptr, nullptr);
   else
     fwd_kernel<BS, D, false><<<p.R, C::THREADS, 0, s>>>(
         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), mask->row_ptr,
         mask->col_idx, mask->capacity, static_cast<__bf16*>(o), lse, mass, mass ? w.part : nullptr, nullptr, p.N,
-        p.nb, scale, w.order, t0);
+        p.nb, scale, w.order, t0, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -651,8 +832,8 @@ hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, c
                                hipStream_t s) {
   if (p.bs == 128 && p.D == 128) return launch_bs_d<128, 128>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
   if (p.bs == 128 && p.D == 64) return launch_bs_d<128, 64>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
-  if (p.bs == 64 && p.D == 128) return launch_bs_d<64, 128>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
-  return launch_bs_d<64, 64>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
+  if (p.bs == 64 && p.D == 128) return launch_pairs<128>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
+  return launch_pairs<64>(p, q, k, v, scale, mask, o, lse, mass, o32, w, s);
 }
 
 ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void* ws, size_t* bytes) {
@@ -660,6 +841,10 @@ ForwardWs carve_forward(const Problem& p, int64_t capacity, bool want_mass, void
   ForwardWs w{};
   if (want_mass) w.part = c.take<float>((size_t)capacity * p.bs);
   if (p.dtype == BSA_BF16) w.order = c.take<int32_t>(tail_rows(p.R));
+  if (p.dtype == BSA_BF16 && p.bs == 64) {   // the pair grid's unit lists
+    w.units = c.take<uint32_t>((size_t)capacity);
+    w.ulen = c.take<int32_t>((size_t)p.B * p.H * ((p.nb + 1) / 2));
+  }
   *bytes = align_up(c.off, 256);
   return w;
 }

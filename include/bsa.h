@@ -248,7 +248,11 @@ bsa_status bsa_permute_rows(int64_t heads, int32_t n, int32_t row_bytes, const v
 /* Sparse attention forward over a block mask (see the header comment, stage 2).
  *   q, k, v    [B,H,N,D] device tensors of shape->dtype.
  *   scale      logit scale; <= 0 selects 1/sqrt(D).
- *   mask       CSR over the R rows (e.g. from bsa_estimate_mask).
+ *   mask       CSR over the R rows (e.g. from bsa_estimate_mask).  Each row's
+ *              entries are attended as listed.  With block 64 (bf16) rows 2m
+ *              and 2m + 1 must be adjacent in col_idx (a non-decreasing
+ *              row_ptr, as every CSR this library writes); a pair of rows
+ *              that is not gets no entries.
  *   o          [B,H,N,D] output of shape->dtype: softmax(scale*Q_i K_S^T) V_S
  *              over the keys S of the row's selected blocks.
  *   lse        [B,H,N] fp32 output: natural log of sum over S of exp(scale*q.k).
