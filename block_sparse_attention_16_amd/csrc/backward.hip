@@ -295,14 +295,21 @@ __global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restr
 // kernel; the last pass forms dS^T = P^T (dP^T - delta_q) and
 // dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
-template <int BS, int D>
+// PAIR (64-token blocks): as in the forward, a 128-query workgroup takes the
+// mask rows of query blocks 2m and 2m + 1 (waves 0-1 and 2-3) and walks the
+// pair's unit list (64-key blocks flagged with the rows that list them); a
+// wave takes P = 0 on a unit its row does not list, which adds exact zeros.
+template <int BS, int D, bool PAIR = false>
 __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, float* __restrict__ delta, const float* __restrict__ lse2,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t cap,
     __bf16* __restrict__ dq, int N, int nb, float scale, int delta_given, const int32_t* __restrict__ order,
-    int t0) {
+    int t0, const uint32_t* __restrict__ units, const int32_t* __restrict__ ulen) {
   using C = BCfg<BS, D>;
+  static_assert(!PAIR || BS == 128, "a pair of 64-token query blocks fills a 128-query workgroup");
+  constexpr int KB = PAIR ? 64 : BS;          // tokens per key block and per mask row's query block
+  constexpr int UPE = PAIR ? 1 : C::U;        // units per listed key block
   __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
@@ -310,21 +317,33 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
 
   // head-major rows up to t0, the grid's last rows longest first (order)
   const int r = (int)blockIdx.x < t0 ? (int)blockIdx.x : order[blockIdx.x - t0];
-  const int bh = r / nb, i = r - bh * nb;
+  const int nbw = PAIR ? (nb + 1) / 2 : nb;  // workgroup rows per head
+  const int bh = r / nbw, i = r - bh * nbw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int qloc = wave * 32 + l32;
   const int qq = i * BS + qloc;
-  int64_t e_begin = row_ptr[r], e_end = row_ptr[r + 1];
-  if (e_end > cap) e_end = cap;
-  if (e_begin < 0) e_begin = 0;
-  if (e_begin > e_end) e_begin = e_end;
-  const int n_e = (int)(e_end - e_begin);
-  const int n_u = n_e * C::U;
+  const int wrow = PAIR ? (wave >> 1) : 0;    // pair: row 2i (waves 0-1) or 2i + 1 (waves 2-3)
+  const bool row_ok = !PAIR || 2 * i + wrow < nb;
+  const int32_t* ids;                          // unit ids: the row's entries or the pair's unit list
+  int n_u;
+  if constexpr (PAIR) {
+    int64_t a = row_ptr[(int64_t)bh * nb + 2 * i];
+    a = a < 0 ? 0 : (a > cap ? cap : a);
+    ids = reinterpret_cast<const int32_t*>(units) + a;
+    n_u = ulen[r];
+  } else {
+    int64_t e_begin = row_ptr[r], e_end = row_ptr[r + 1];
+    if (e_end > cap) e_end = cap;
+    if (e_begin < 0) e_begin = 0;
+    if (e_begin > e_end) e_begin = e_end;
+    ids = col_idx + e_begin;
+    n_u = (int)(e_end - e_begin) * C::U;
+  }
   const auto kh = raw_rsrc(k + (size_t)bh * N * D, N * D * 2);
   const auto vh = raw_rsrc(v + (size_t)bh * N * D, N * D * 2);
-  const auto colr = raw_rsrc(col_idx + e_begin, n_e * 4);
+  const auto colr = raw_rsrc(ids, (n_u / UPE) * 4);
 
   bf16x8 qf[C::DS], gf[C::DS];     // Q^T and dO^T as B operands (query column qloc)
   {
@@ -335,8 +354,8 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
       gf[ds] = *reinterpret_cast<const bf16x8*>(dout + ((size_t)bh * N + qr) * D + ds * 16 + hf * 8);
     }
   }
-  const size_t prow = (size_t)bh * nb * BS + (size_t)i * BS + qloc;   // padded per-head row
-  const float my_lse2 = lse2[prow];     // +inf for padding queries -> P = 0
+  const size_t prow = (size_t)bh * nb * KB + qq;   // padded per-head row
+  const float my_lse2 = row_ok ? lse2[prow] : INFINITY;   // +inf for padding queries -> P = 0
   const float c2 = scale * kLog2e;
   float my_delta = 0.f;
 
@@ -350,21 +369,27 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
-  // first key and valid-key count of unit u from its block id
+  // first key and valid-key count of unit u from its block id (pair: 0 keys
+  // for a unit this wave's row does not list)
   auto unit_key = [&](int j_raw, int u, int& nvk) {
+    bool mine = true;
+    if constexpr (PAIR) {
+      mine = (((uint32_t)j_raw >> (30 + wrow)) & 1u) != 0u;
+      j_raw &= 0x3fffffff;
+    }
     const bool valid = j_raw >= 0 && j_raw < nb;
-    const int key0 = (valid ? j_raw : 0) * BS + (u % C::U) * C::SUB;
-    nvk = valid ? max(0, min(C::SUB, N - key0)) : 0;
+    const int key0 = (valid ? j_raw : 0) * KB + (u % UPE) * C::SUB;
+    nvk = valid && mine ? max(0, min(C::SUB, N - key0)) : 0;
     return key0;
   };
-  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / C::U) * 4, 0, 0); };
+  auto col_load = [&](int u) { return __builtin_amdgcn_raw_buffer_load_b32(colr, (u / UPE) * 4, 0, 0); };
 
   // SECOND = false: accumulate sum_k P dP into dsum; true: dS and dQ.
   auto pass = [&](auto second, float& dsum) __attribute__((always_inline)) {
     constexpr bool SECOND = decltype(second)::value;
     int jv0 = 0, jv1 = 0;
     if (n_u > 0) {
-      jv0 = col_idx[e_begin];
+      jv0 = ids[0];
       int nv;
       dma_tiles<BS, D>(kh, vh, unit_key(jv0, 0, nv), k0s, v0s, wave, off);
       jv1 = col_load(1);
@@ -421,11 +446,11 @@ __global__ __launch_bounds__(2 * BS, 2) void dq_kernel(
   using second_t = std::integral_constant<bool, true>;
   float dsum = 0.f;
   if (delta_given) {
-    my_delta = delta[prow];
+    my_delta = row_ok ? delta[prow] : 0.f;
   } else {
     pass(first_t{}, dsum);
     my_delta = dsum + __shfl_xor(dsum, 32);
-    if (hf == 0) delta[prow] = my_delta;
+    if (hf == 0 && row_ok) delta[prow] = my_delta;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // the last unit's prefetched id
     __syncthreads();                      // every wave is done with the tiles
   }
@@ -691,15 +716,27 @@ template <int BS, int D>
 hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v, const void* d_o,
                            float scale, const bsa_csr* mask, void* dq, void* dk, void* dv, bool delta_given,
                            const BackwardWs& w, hipStream_t s) {
-  const int Tq = query_tail_rows(p.R, BS), t0 = p.R - Tq;   // dQ grid: rows
   const int Tk = tail_rows(p.R), t0k = p.R - Tk;              // dK/dV grid: columns
-  launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, Tq, w.order_q, s);
   launch_tail_order(nullptr, 0, w.csc_count, t0k, Tk, w.order_k, s);
-  dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-      static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
-      static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0,   // writes delta when not given
-      w.order_q, t0);
+  if constexpr (BS == 64) {                                   // dQ grid: pairs of rows
+    const int P = p.B * p.H * ((p.nb + 1) / 2);
+    launch_pair_units(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, P, w.units, w.ulen, s);
+    const int Tq = tail_rows(P), t0 = P - Tq;
+    launch_tail_order(nullptr, 0, w.ulen, t0, Tq, w.order_q, s);
+    dq_kernel<128, D, true><<<P, 256, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+        static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
+        static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0,   // writes delta when not given
+        w.order_q, t0, w.units, w.ulen);
+  } else {                                                    // dQ grid: rows
+    const int Tq = query_tail_rows(p.R, BS), t0 = p.R - Tq;
+    launch_tail_order(mask->row_ptr, mask->capacity, nullptr, t0, Tq, w.order_q, s);
+    dq_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
+        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+        static_cast<const __bf16*>(d_o), w.delta, w.lse2, mask->row_ptr, mask->col_idx, mask->capacity,
+        static_cast<__bf16*>(dq), p.N, p.nb, scale, delta_given ? 1 : 0,   // writes delta when not given
+        w.order_q, t0, nullptr, nullptr);
+  }
   dkv_kernel<BS, D><<<p.R, 2 * BS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(d_o), w.delta, w.lse2, w.csc_start, w.csc_count, w.csc_row,
@@ -736,6 +773,10 @@ BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* 
   if (p.dtype == BSA_BF16) {
     w.order_q = c.take<int32_t>(tail_rows(p.R));
     w.order_k = c.take<int32_t>(tail_rows(p.R));
+  }
+  if (p.dtype == BSA_BF16 && p.bs == 64) {   // the dQ pair grid's unit lists
+    w.units = c.take<uint32_t>((size_t)(capacity > 0 ? capacity : 1));
+    w.ulen = c.take<int32_t>((size_t)p.B * p.H * ((p.nb + 1) / 2));
   }
   *bytes = align_up(c.off, 256);
   return w;

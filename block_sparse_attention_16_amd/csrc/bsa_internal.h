@@ -85,6 +85,10 @@ inline int tail_rows(int R) { return R < kTailRows ? R : kTailRows; }
 inline int query_tail_rows(int R, int bs) { return bs == 64 ? (R < 1024 ? R : 1024) : tail_rows(R); }
 // Lengths are counts[r] when counts is non-null, else the CSR extents of
 // row_ptr clamped to [0, cap].
+// Unit lists of the pair grid for 64-token blocks (forward_bf16.hip): P =
+// B*H*ceil(nb/2) pairs of rows; units [capacity], ulen [P].
+void launch_pair_units(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap, int nb, int P, uint32_t* units,
+                       int32_t* ulen, hipStream_t s);
 void launch_tail_order(const int32_t* row_ptr, int64_t cap, const int32_t* counts, int r0, int T, int32_t* order,
                        hipStream_t s);
 
@@ -112,6 +116,8 @@ struct BackwardWs {
   int32_t* csc_row;    // [capacity] query block of each transposed entry
   int32_t* order_q;    // [tail_rows(R)] dQ grid's last rows, longest first
   int32_t* order_k;    // [tail_rows(R)] dK/dV grid's last columns, longest first
+  uint32_t* units;     // bf16, block 64: [capacity] unit lists of the dQ pair grid
+  int32_t* ulen;       // bf16, block 64: [B*H*ceil(nb/2)] their lengths
 };
 BackwardWs carve_backward(const Problem& p, int64_t capacity, void* ws, size_t* bytes);
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const void* o,

@@ -788,8 +788,7 @@ hipError_t launch_pairs(const Problem& p, const void* q, const void* k, const vo
                         hipStream_t s) {
   using C = Cfg<128, D>;
   const int P = p.B * p.H * ((p.nb + 1) / 2);
-  pair_units_kernel<<<(P + kPairWaves - 1) / kPairWaves, 64 * kPairWaves, 0, s>>>(
-      mask->row_ptr, mask->col_idx, mask->capacity, p.nb, P, w.units, w.ulen);
+  launch_pair_units(mask->row_ptr, mask->col_idx, mask->capacity, p.nb, P, w.units, w.ulen, s);
   const int T = tail_rows(P), t0 = P - T;
   launch_tail_order(nullptr, 0, w.ulen, t0, T, w.order, s);
   if (o32 != nullptr)
@@ -826,6 +825,13 @@ hipError_t launch_bs_d(const Problem& p, const void* q, const void* k, const voi
 }
 
 }  // namespace
+
+void launch_pair_units(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap, int nb, int P, uint32_t* units,
+                       int32_t* ulen, hipStream_t s) {
+  if (P > 0)
+    pair_units_kernel<<<(P + kPairWaves - 1) / kPairWaves, 64 * kPairWaves, 0, s>>>(row_ptr, col_idx, cap, nb, P,
+                                                                                     units, ulen);
+}
 
 hipError_t launch_forward_bf16(const Problem& p, const void* q, const void* k, const void* v, float scale,
                                const bsa_csr* mask, void* o, float* lse, float* mass, float* o32, const ForwardWs& w,
