@@ -139,3 +139,28 @@ def test_pair_grid_rows_independent_bitwise(bsa, D):
         assert torch.equal(o1[0, bh, lo:hi], o2[0, bh, lo:hi]), f"row {r}: O depends on the neighbour row"
         assert torch.equal(l1[0, bh, lo:hi], l2[0, bh, lo:hi]), f"row {r}: LSE depends on the neighbour row"
         assert torch.equal(m1[rp1[r]:rp1[r + 1]], m2[rp2[r]:rp2[r + 1]]), f"row {r}: block mass"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pair_grid_entries_past_capacity(bsa, D):
+    """A capacity that ends inside a row: that row keeps its entries below the
+    capacity, later rows have none (their O is 0, their LSE -inf), as in the
+    single-row grid of 128-token blocks."""
+    rng = np.random.default_rng(13 + D)
+    B, H, N = 1, 2, 11 * BS - 9
+    nb = O.num_blocks(N, BS)
+    q, k, v = _inputs(rng, B, H, N, D)
+    rows = [np.sort(rng.choice(nb, size=int(rng.integers(2, nb + 1)), replace=False)) for _ in range(B * H * nb)]
+    rp, ci = O.rows_to_csr(rows)
+    cut = nb + 3                              # a row of the second head, counted from its first row
+    cap = int(rp[cut] + (rp[cut + 1] - rp[cut]) // 2)
+    mask = bsa.csr_from_host(rp, ci, "cuda", capacity=cap)
+    qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
+    o, lse, mass = bsa.bsa_forward(qd, kd, vd, mask, BS)
+    torch.cuda.synchronize()
+    clipped = [ci[rp[r]:min(rp[r + 1], cap)] if rp[r] < cap else np.zeros(0, np.int64) for r in range(len(rows))]
+    crp, cci = O.rows_to_csr(clipped)
+    assert crp[-1] == cap
+    err = compare_forward(q, k, v, BS, crp, cci, default_scale(D), list(range(B * H * nb)), to_host(o),
+                          to_host(lse), to_host(mass)[:cap], "bf16")
+    assert_forward_within(err, "bf16", f"capacity cut D={D}")
