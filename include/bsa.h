@@ -270,7 +270,9 @@ bsa_status bsa_forward(const bsa_shape* shape, const void* q, const void* k, con
                        float* block_mass, float* o_f32, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the sparse forward for a loss L with dL/dO = d_o.
- *   o, lse     the forward's outputs for the same q, k, v, scale and mask.
+ *   o, lse     the forward's outputs for the same q, k, v, scale and mask
+ *              (the same conditions on the mask: with block 64, bf16, rows
+ *              2m and 2m + 1 adjacent in col_idx).
  *   o_f32      NULL, or (BSA_BF16 only) the forward's o_f32 output: then
  *              delta_q = dO_q . O_q is taken from it and dQ needs one pass
  *              over the row.  With NULL (or for BSA_FP32 data) delta is
