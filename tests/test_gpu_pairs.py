@@ -164,3 +164,25 @@ def test_pair_grid_entries_past_capacity(bsa, D):
     err = compare_forward(q, k, v, BS, crp, cci, default_scale(D), list(range(B * H * nb)), to_host(o),
                           to_host(lse), to_host(mass)[:cap], "bf16")
     assert_forward_within(err, "bf16", f"capacity cut D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pair_grid_mask_with_no_entries(bsa, D):
+    """A mask with no entries at all (capacity 0): every query gets O = 0 and
+    LSE = -inf, and the backward gives zero gradients."""
+    rng = np.random.default_rng(3 + D)
+    B, H, N = 1, 2, 5 * BS - 7
+    nb = O.num_blocks(N, BS)
+    q, k, v = _inputs(rng, B, H, N, D)
+    rp = np.zeros(B * H * nb + 1, np.int64)
+    mask = bsa.csr_from_host(rp, np.zeros(0, np.int64), "cuda")
+    assert mask.capacity == 0
+    qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
+    o32 = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    o, lse, _ = bsa.bsa_forward(qd, kd, vd, mask, BS, want_mass=False, o32=o32)
+    g = to_device(round_to_bf16(rng.normal(size=(B, H, N, D)).astype(np.float32)), "bf16")
+    dq, dk, dv = bsa.bsa_backward(qd, kd, vd, o, g, lse, mask, BS, o32=o32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(o32 == 0)
+    assert torch.all(torch.isneginf(lse))
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
